@@ -1,0 +1,67 @@
+"""The seeded generator: shapes, dtypes, reproducibility and cache validity."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workload
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_shapes_dtypes_and_cache_validity(cid):
+    cfg = workload.config(cid)
+    H, W, idx, logp = workload.make_inputs(cfg)
+    assert H.shape == (cfg.N, cfg.d) and W.shape == (cfg.V, cfg.d)
+    assert idx.shape == (cfg.N, cfg.K) and logp.shape == (cfg.N, cfg.K)
+    want = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    assert H.dtype == want and W.dtype == want
+    assert idx.dtype == torch.int32 and logp.dtype == torch.float32
+    i = idx.numpy()
+    assert i.min() >= 0 and i.max() < cfg.V
+    s = np.sort(i, axis=1)
+    assert not np.any(s[:, 1:] == s[:, :-1]), "indices must be distinct per row"
+    lp = logp.numpy()
+    assert np.all(lp <= 0) and np.all(np.isfinite(lp))
+    assert np.all(np.diff(lp, axis=1) <= 0), "cache is sorted by descending teacher log-prob"
+    mass = np.exp(lp.astype(np.float64)).sum(axis=1)
+    assert np.all(mass <= 1.0 + 1e-6) and np.all(mass > 0)
+
+
+def test_reproducible_and_distinct_seeds():
+    a = workload.make_inputs(workload.config(1))
+    b = workload.make_inputs(workload.config(1))
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    c = workload.make_inputs(workload.config(1, N=64))
+    assert torch.equal(a[1], c[1])  # W depends on the config id only
+
+
+def test_statistics_of_tiny_config():
+    cfg = workload.config(1)
+    H, W, idx, logp = workload.make_inputs(cfg)
+    assert abs(H.float().std().item() - 1.0) < 0.05
+    assert abs(W.float().std().item() * math.sqrt(cfg.d) - 1.0) < 0.05
+
+
+def test_sweep_points_get_their_own_seeds():
+    s1 = workload._seeds(workload.config(4, N=32768))
+    s2 = workload._seeds(workload.config(4, N=65536))
+    assert s1 != s2
+
+
+def test_bf16_inputs_are_rounded_and_teacher_uses_rounded_h():
+    cfg = workload.config(2, N=16)
+    H, W, idx, logp = workload.make_inputs(cfg)
+    assert H.dtype == torch.bfloat16
+    sH, sW, sT = workload._seeds(cfg)
+    Wt = workload._normal((cfg.V, cfg.d), 2.0 * cfg.d ** -0.5, sT)
+    i2, l2 = workload.teacher_topk(H.float(), Wt, cfg.K)
+    assert torch.equal(i2, idx) and torch.equal(l2, logp)
+
+
+def test_cache_digest_changes_with_content():
+    H, W, idx, logp = workload.make_inputs(workload.config(1))
+    d1 = workload.cache_digest(idx, logp)
+    logp2 = logp.clone(); logp2[0, 0] -= 1e-3
+    assert d1 != workload.cache_digest(idx, logp2)
