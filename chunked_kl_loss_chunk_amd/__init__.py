@@ -1,0 +1,16 @@
+"""Fused, chunked top-K KL distillation loss for AMD MI355X (gfx950).
+
+The loss, its forward and its backward run in the HIP kernels of the in-tree
+library ``libkdkl.so`` (C ABI: include/kd_fused_kl.h). This package only
+marshals arguments; PyTorch provides device memory and streams.
+"""
+from ._build import LIB_PATH, build  # noqa: F401
+from ._lib import KDError, lib, status_str  # noqa: F401
+from .ops import (  # noqa: F401
+    FusedTopKKL,
+    cast_f32_to_bf16,
+    fused_kl,
+    kl_backward,
+    kl_forward,
+    workspace_bytes,
+)

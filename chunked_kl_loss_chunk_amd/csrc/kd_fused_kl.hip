@@ -1,0 +1,809 @@
+// kd_fused_kl.hip — kernels, chunk scheduler and C entry points of the fused,
+// chunked top-K KL distillation loss for MI355X (gfx950).
+//
+// Source pages (cited by title and section):
+//  [P1] "Distilação de LLMs mais barata: top-K offline e KL fundida cortam
+//       VRAM em até 15x" (imasters.com.br)
+//  [P4] "Hugging Face：让知识蒸馏廉价到可大规模运行" (feinterview.poetries.top)
+//  [P5] "Chunkovaná KL strata umožnila destilovať LLM s 32-tisícovým
+//       kontextom na jednom H200" (aifeed.sk)
+//
+// Per chunk of C positions ([P1] "As duas mudanças"; [P4] 为什么蒸馏恢复代价高昂,
+// "Fused chunked KL" paragraph: project one chunk, fold it into the running
+// loss, discard it; recompute it in backward):
+//
+//  forward   prep    bucket the chunk's top-K entries by logit tile
+//            logits  z tile = H_c Wᵀ on MFMA; per tile: row max and Σexp
+//                    (online logsumexp partials) and z at the cached ids
+//            combine lse_r from the partials; L_r = Σp·logp − Σp·z + S_r·lse_r
+//  backward  prep    as above, plus S_r = Σ_k p_rk
+//            dlogits recompute the z tile; dl = g (S_r e^{z−lse_r} − p_sparse)
+//                    in registers; write the chunk's dl once (bf16 or fp32)
+//            dH      dH_c = dl · W      (split over the vocabulary)
+//            dW      dW  += dlᵀ · H_c   (fp32 read-modify-write, chunk order fixed)
+//
+// The teacher distribution stays sparse and is not renormalised ([P5] "Čo
+// dopĺňajú podrobnejšie experimenty"). The gradient is the closed form of the
+// dense KL: ∂L_r/∂z_rj = S_r q_rj − p_rj (the pages name a closed-form
+// gradient without printing it; [P4] 得到的 student).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "kd_fused_kl.h"
+#include "kd_gemm.h"
+#include "kd_plan.h"
+
+namespace kd {
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+
+template <bool BF16>
+struct Elt;
+template <>
+struct Elt<true> {
+  typedef __bf16 T;
+  static constexpr int size = 2;
+};
+template <>
+struct Elt<false> {
+  typedef float T;
+  static constexpr int size = 4;
+};
+
+// Hit record of one cached teacher entry inside a logit tile.
+__device__ __forceinline__ uint32_t pack_hit(int row_in_tile, int col_in_tile, int k) {
+  return uint32_t(row_in_tile) | (uint32_t(col_in_tile) << 8) | (uint32_t(k) << 18);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Merge two (max, Σexp(x − max)) pairs of an online logsumexp.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == kNegInf) {
+    m = mn;
+    s = 0.f;
+    return;
+  }
+  s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
+  m = mn;
+}
+
+// --------------------------------------------------------------------------
+// small utility kernels
+// --------------------------------------------------------------------------
+__global__ void k_fill_i32(int* __restrict__ p, int64_t n, int v) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void k_fill_f32(float* __restrict__ p, int64_t n, float v) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+__global__ void k_cast_f32_bf16(const float* __restrict__ src, __bf16* __restrict__ dst, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x)
+    dst[i] = __bf16(src[i]);
+}
+
+// Σ x[0..n) in a fixed order: contiguous per-thread ranges, then a tree.
+__global__ __launch_bounds__(1024) void k_sum_fixed(const float* __restrict__ x, int64_t n,
+                                                    float* __restrict__ out) {
+  __shared__ float sh[1024];
+  const int t = threadIdx.x;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t b = t * per, e = b + per < n ? b + per : n;
+  float s = 0.f;
+  for (int64_t i = b; i < e; ++i) s += x[i];
+  sh[t] = s;
+  __syncthreads();
+  for (int w = 512; w >= 1; w >>= 1) {
+    if (t < w) sh[t] += sh[t + w];
+    __syncthreads();
+  }
+  if (t == 0) out[0] = sh[0];
+}
+
+// --------------------------------------------------------------------------
+// prep: bucket the chunk's cached entries by (row tile, vocabulary tile)
+// --------------------------------------------------------------------------
+// One wave per row. Counts valid entries per bucket and writes S_r = Σ_k p_rk.
+// Ids outside [0, V) raise `flag` and are skipped; p = 0 entries are skipped.
+__global__ __launch_bounds__(256) void k_prep_count(const int* __restrict__ idx,
+                                                    const float* __restrict__ logp, int64_t r0,
+                                                    int rows, int K, int V, int nVt,
+                                                    int* __restrict__ counts,
+                                                    float* __restrict__ rowS,
+                                                    int* __restrict__ flag) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int* ir = idx + (r0 + row) * K;
+  const float* lr = logp + (r0 + row) * K;
+  float s = 0.f;
+  for (int k = lane; k < K; k += 64) {
+    const int j = ir[k];
+    const float p = __expf(lr[k]);
+    const bool ok = j >= 0 && j < V;
+    if (!ok) atomicOr(flag, 1);
+    if (ok && p > 0.f) {
+      s += p;
+      atomicAdd(&counts[(row / kTileM) * nVt + j / kTileN], 1);
+    }
+  }
+  s = wave_sum(s);
+  if (lane == 0) rowS[row] = s;
+}
+
+// Exclusive scan of the bucket counts (one workgroup).
+__global__ __launch_bounds__(1024) void k_prep_scan(const int* __restrict__ counts,
+                                                    int* __restrict__ offsets, int nb) {
+  __shared__ int sh[1024];
+  const int t = threadIdx.x;
+  const int per = (nb + 1023) / 1024;
+  const int b = t * per, e = b + per < nb ? b + per : nb;
+  int s = 0;
+  for (int i = b; i < e; ++i) s += counts[i];
+  sh[t] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = t >= off ? sh[t - off] : 0;
+    __syncthreads();
+    sh[t] += v;
+    __syncthreads();
+  }
+  int base = sh[t] - s;
+  for (int i = b; i < e; ++i) {
+    offsets[i] = base;
+    base += counts[i];
+  }
+  if (t == 1023) offsets[nb] = sh[1023];
+}
+
+// Scatter hit records into their buckets. Counting down leaves `counts` at
+// zero for the next chunk. The order inside a bucket does not matter: every
+// record touches a distinct output element.
+__global__ __launch_bounds__(256) void k_prep_scatter(const int* __restrict__ idx,
+                                                      const float* __restrict__ logp, int64_t r0,
+                                                      int rows, int K, int V, int nVt,
+                                                      int* __restrict__ counts,
+                                                      const int* __restrict__ offsets,
+                                                      uint2* __restrict__ recs) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int* ir = idx + (r0 + row) * K;
+  const float* lr = logp + (r0 + row) * K;
+  for (int k = lane; k < K; k += 64) {
+    const int j = ir[k];
+    const float p = __expf(lr[k]);
+    if (j >= 0 && j < V && p > 0.f) {
+      const int b = (row / kTileM) * nVt + j / kTileN;
+      const int pos = offsets[b] + atomicSub(&counts[b], 1) - 1;
+      recs[pos] = make_uint2(pack_hit(row % kTileM, j % kTileN, k), __float_as_uint(p));
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// forward: fused logit tile with online-logsumexp partials and top-K gather
+// --------------------------------------------------------------------------
+struct FwdArgs {
+  RowOp H;  // chunk rows of H
+  RowOp W;
+  int kt;   // stages along d
+  int tiles_m, tiles_n;
+  int rows, V, K, nVt;
+  const int* offsets;
+  const uint2* recs;
+  float* zhit;     // [C, K]: z at the cached ids
+  float2* part;    // [C_pad, nVt]: (max, Σexp) of each row over each tile
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_fwd_logits(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  const int nblk = a.tiles_m * a.tiles_n;
+  const int logical = xcd_logical(blockIdx.x, nblk);
+  const int tm_t = logical % a.tiles_m, tn_t = logical / a.tiles_m;
+  const int m_base = tm_t * kBM, n_base = tn_t * kBN;
+
+  Acc acc;
+  gemm_tile<BF16, RowLoader<kBM>, RowOp, RowLoader<kBN>, RowOp>(acc, a.H, m_base, a.W, n_base, 0,
+                                                                 a.kt, smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % kWM, wn = wave / kWM;
+
+  // z at the cached teacher ids that fall in this tile.
+  const int bkt = tm_t * a.nVt + tn_t;
+  const int h0 = a.offsets[bkt], h1 = a.offsets[bkt + 1];
+  for (int h = h0; h < h1; ++h) {
+    const uint2 r = a.recs[h];
+    const int rl = r.x & 255, cl = (r.x >> 8) & 1023, k = int(r.x >> 18);
+    const int wr = rl - wm * kWTM, wc = cl - wn * kWTN;
+    if (unsigned(wr) >= unsigned(kWTM) || unsigned(wc) >= unsigned(kWTN)) continue;
+    int owner, sel;
+    acc_owner(wr, wc, &owner, &sel);
+    const float z = acc_get(acc, sel);
+    if (lane == owner) a.zhit[int64_t(m_base + rl) * a.K + k] = z;
+  }
+
+  // Row max and Σexp over this tile's valid columns; lanes of one half share rows.
+  float2* red = reinterpret_cast<float2*>(smem);  // [kWN][kBM]
+  bool colok[kTN];
+#pragma unroll
+  for (int b = 0; b < kTN; ++b) colok[b] = n_base + acc_col(wn, b, lane) < a.V;
+#pragma unroll
+  for (int tm = 0; tm < kTM; ++tm) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float m = kNegInf;
+#pragma unroll
+      for (int b = 0; b < kTN; ++b) m = colok[b] ? fmaxf(m, acc[tm][b][i]) : m;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      const float ms = m == kNegInf ? 0.f : m;
+      float s = 0.f;
+#pragma unroll
+      for (int b = 0; b < kTN; ++b) s += colok[b] ? __expf(acc[tm][b][i] - ms) : 0.f;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+      if ((lane & 31) == 0) red[wn * kBM + acc_row(wm, tm, i, lane)] = make_float2(m, s);
+    }
+  }
+  __syncthreads();
+  if (tid < kBM && m_base + tid < a.rows) {
+    float m = red[tid].x, s = red[tid].y;
+#pragma unroll
+    for (int w = 1; w < kWN; ++w) lse_merge(m, s, red[w * kBM + tid].x, red[w * kBM + tid].y);
+    a.part[int64_t(m_base + tid) * a.nVt + tn_t] = make_float2(m, s);
+  }
+}
+
+// One wave per row: lse_r from the tile partials (fixed order), then
+// L_r = Σ_k p_k logp_k − Σ_k p_k z_k + S_r lse_r.
+__global__ __launch_bounds__(256) void k_fwd_combine(const float2* __restrict__ part, int nVt,
+                                                     const float* __restrict__ zhit,
+                                                     const int* __restrict__ idx,
+                                                     const float* __restrict__ logp, int64_t r0,
+                                                     int rows, int K, int V,
+                                                     float* __restrict__ lse_out,
+                                                     float* __restrict__ loss_out) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float m = kNegInf, s = 0.f;
+  const float2* pr = part + int64_t(row) * nVt;
+  for (int t = lane; t < nVt; t += 64) {
+    const float2 v = pr[t];
+    lse_merge(m, s, v.x, v.y);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
+    lse_merge(m, s, m2, s2);
+  }
+  const float lse = m + __logf(s);
+  const int* ir = idx + (r0 + row) * K;
+  const float* lr = logp + (r0 + row) * K;
+  const float* zr = zhit + int64_t(row) * K;
+  float A = 0.f, B = 0.f, S = 0.f;
+  for (int k = lane; k < K; k += 64) {
+    const int j = ir[k];
+    const float lp = lr[k];
+    const float p = __expf(lp);
+    if (j >= 0 && j < V && p > 0.f) {
+      S += p;
+      A += p * lp;
+      B += p * zr[k];
+    }
+  }
+  A = wave_sum(A);
+  B = wave_sum(B);
+  S = wave_sum(S);
+  if (lane == 0) {
+    lse_out[r0 + row] = lse;
+    loss_out[r0 + row] = A - B + S * lse;
+  }
+}
+
+// --------------------------------------------------------------------------
+// backward: recompute the logit tile and turn it into dlogits in registers
+// --------------------------------------------------------------------------
+struct DlArgs {
+  RowOp H;
+  RowOp W;
+  int kt;
+  int tiles_m, tiles_n;
+  int rows, V, nVt;
+  const int* offsets;
+  const uint2* recs;
+  const float* lse;   // chunk's lse (forward output)
+  const float* rowS;  // chunk's S_r
+  const float* grad;  // device scalar g
+  void* dl;           // [C_pad, V_pad] of the compute dtype
+  int64_t ld_dl;      // elements
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs a) {
+  typedef typename Elt<BF16>::T T;
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  const int nblk = a.tiles_m * a.tiles_n;
+  const int logical = xcd_logical(blockIdx.x, nblk);
+  const int tm_t = logical % a.tiles_m, tn_t = logical / a.tiles_m;
+  const int m_base = tm_t * kBM, n_base = tn_t * kBN;
+
+  Acc acc;
+  gemm_tile<BF16, RowLoader<kBM>, RowOp, RowLoader<kBN>, RowOp>(acc, a.H, m_base, a.W, n_base, 0,
+                                                                 a.kt, smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % kWM, wn = wave / kWM;
+  const float g = *a.grad;
+
+  bool colok[kTN];
+#pragma unroll
+  for (int b = 0; b < kTN; ++b) colok[b] = n_base + acc_col(wn, b, lane) < a.V;
+#pragma unroll
+  for (int tm = 0; tm < kTM; ++tm) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = m_base + acc_row(wm, tm, i, lane);
+      const bool rok = row < a.rows;
+      const float l = rok ? a.lse[row] : 0.f;
+      const float gs = rok ? g * a.rowS[row] : 0.f;
+#pragma unroll
+      for (int b = 0; b < kTN; ++b)
+        acc[tm][b][i] = (rok && colok[b]) ? gs * __expf(acc[tm][b][i] - l) : 0.f;
+    }
+  }
+
+  // Subtract g·p at the cached ids of this tile.
+  const int bkt = tm_t * a.nVt + tn_t;
+  const int h0 = a.offsets[bkt], h1 = a.offsets[bkt + 1];
+  for (int h = h0; h < h1; ++h) {
+    const uint2 r = a.recs[h];
+    const int rl = r.x & 255, cl = (r.x >> 8) & 1023;
+    const int wr = rl - wm * kWTM, wc = cl - wn * kWTN;
+    if (unsigned(wr) >= unsigned(kWTM) || unsigned(wc) >= unsigned(kWTN)) continue;
+    int owner, sel;
+    acc_owner(wr, wc, &owner, &sel);
+    acc_sub(acc, sel, lane == owner ? g * __uint_as_float(r.y) : 0.f);
+  }
+
+  T* dl = reinterpret_cast<T*>(a.dl);
+#pragma unroll
+  for (int tm = 0; tm < kTM; ++tm)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t row = m_base + acc_row(wm, tm, i, lane);
+#pragma unroll
+      for (int b = 0; b < kTN; ++b) dl[row * a.ld_dl + n_base + acc_col(wn, b, lane)] = T(acc[tm][b][i]);
+    }
+}
+
+// --------------------------------------------------------------------------
+// dH = dl · W   (A = dl [C_pad, V_pad] rows; B = W [V, d] as [K][cols])
+// --------------------------------------------------------------------------
+struct DhArgs {
+  RowOp dl;
+  ColOp W;
+  int tiles_m, tiles_n, splits, kt_total;
+  int rows, d;
+  void* dH;          // chunk rows of dH, used when splits == 1
+  float* part;       // [splits, C_pad, d] fp32 partials, used when splits > 1
+  int64_t part_stride;
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_bwd_dh(DhArgs a) {
+  typedef typename Elt<BF16>::T T;
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  const int nblk = a.tiles_m * a.tiles_n * a.splits;
+  const int logical = xcd_logical(blockIdx.x, nblk);
+  const int tm_t = logical % a.tiles_m;
+  const int rest = logical / a.tiles_m;
+  const int tn_t = rest % a.tiles_n, split = rest / a.tiles_n;
+  const int kt0 = int(int64_t(split) * a.kt_total / a.splits);
+  const int kt1 = int(int64_t(split + 1) * a.kt_total / a.splits);
+  const int m_base = tm_t * kBM, n_base = tn_t * kBN;
+
+  Acc acc;
+  gemm_tile<BF16, RowLoader<kBM>, RowOp, ColLoader<BF16, kBN>, ColOp>(acc, a.dl, m_base, a.W, n_base,
+                                                                      kt0, kt1, smem);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % kWM, wn = wave / kWM;
+#pragma unroll
+  for (int tm = 0; tm < kTM; ++tm)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = m_base + acc_row(wm, tm, i, lane);
+      if (row >= a.rows) continue;
+#pragma unroll
+      for (int b = 0; b < kTN; ++b) {
+        const int col = n_base + acc_col(wn, b, lane);
+        if (col >= a.d) continue;
+        const int64_t o = int64_t(row) * a.d + col;
+        if (a.splits == 1)
+          reinterpret_cast<T*>(a.dH)[o] = T(acc[tm][b][i]);
+        else
+          a.part[split * a.part_stride + o] = acc[tm][b][i];
+      }
+    }
+}
+
+// Sum the dH split partials in split order and write dH.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_bwd_dh_reduce(const float* __restrict__ part, int splits,
+                                                       int64_t stride, int64_t n, void* dH) {
+  typedef typename Elt<BF16>::T T;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    float s = 0.f;
+    for (int sp = 0; sp < splits; ++sp) s += part[sp * stride + i];
+    reinterpret_cast<T*>(dH)[i] = T(s);
+  }
+}
+
+// --------------------------------------------------------------------------
+// dW (+)= dlᵀ · H_c   (A = dl as [K=C][cols=V]; B = H_c as [K=C][cols=d])
+// --------------------------------------------------------------------------
+struct DwArgs {
+  ColOp dl;
+  ColOp H;
+  int tiles_m, tiles_n, kt;
+  int V, d;
+  float* dW;
+  int beta;  // 0: overwrite, 1: accumulate
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_bwd_dw(DwArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  const int nblk = a.tiles_m * a.tiles_n;
+  const int logical = xcd_logical(blockIdx.x, nblk);
+  const int tn_t = logical % a.tiles_n, tm_t = logical / a.tiles_n;
+  const int m_base = tm_t * kBM, n_base = tn_t * kBN;
+
+  Acc acc;
+  gemm_tile<BF16, ColLoader<BF16, kBM>, ColOp, ColLoader<BF16, kBN>, ColOp>(acc, a.dl, m_base, a.H,
+                                                                            n_base, 0, a.kt, smem);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % kWM, wn = wave / kWM;
+#pragma unroll
+  for (int tm = 0; tm < kTM; ++tm)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = m_base + acc_row(wm, tm, i, lane);
+      if (row >= a.V) continue;
+#pragma unroll
+      for (int b = 0; b < kTN; ++b) {
+        const int col = n_base + acc_col(wn, b, lane);
+        if (col >= a.d) continue;
+        float* p = a.dW + int64_t(row) * a.d + col;
+        *p = a.beta ? *p + acc[tm][b][i] : acc[tm][b][i];
+      }
+    }
+}
+
+// --------------------------------------------------------------------------
+// host side: chunk scheduler
+// --------------------------------------------------------------------------
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Ws {
+  char* base;
+  const Plan& p;
+  template <class T>
+  T* at(size_t off) const {
+    return reinterpret_cast<T*>(base + off);
+  }
+};
+
+int launch_status() { return hipGetLastError() == hipSuccess ? KD_OK : KD_ERR_HIP; }
+
+// Optional kernel timing: when enabled, launches are bracketed by HIP events
+// on the caller's stream and read back by kd_timing_read.
+struct TimingRec {
+  int cls;
+  hipEvent_t a, b;
+};
+bool g_timing = false;
+std::vector<hipEvent_t> g_event_pool;
+size_t g_events_used = 0;
+std::vector<TimingRec> g_timing_recs;
+
+hipEvent_t timing_event() {
+  if (g_events_used == g_event_pool.size()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    g_event_pool.push_back(e);
+  }
+  return g_event_pool[g_events_used++];
+}
+
+template <class F>
+void timed(int cls, hipStream_t st, F&& launch) {
+  if (!g_timing) {
+    launch();
+    return;
+  }
+  hipEvent_t a = timing_event(), b = timing_event();
+  if (a) hipEventRecord(a, st);
+  launch();
+  if (b) hipEventRecord(b, st);
+  if (a && b) g_timing_recs.push_back(TimingRec{cls, a, b});
+}
+
+void launch_prep(const Plan& p, const Ws& ws, const int32_t* idx, const float* logp, int64_t r0,
+                 int rows, hipStream_t st) {
+  const int nblk = int(cdiv(rows, 4));
+  timed(KD_KERNEL_PREP, st, [&] {
+    hipLaunchKernelGGL(k_prep_count, dim3(nblk), dim3(256), 0, st, idx, logp, r0, rows, int(p.K),
+                       int(p.V), int(p.nVt), ws.at<int>(p.off_counts), ws.at<float>(p.off_rowS),
+                       ws.at<int>(p.off_flag));
+    hipLaunchKernelGGL(k_prep_scan, dim3(1), dim3(1024), 0, st, ws.at<int>(p.off_counts),
+                       ws.at<int>(p.off_offsets), int(p.nb));
+    hipLaunchKernelGGL(k_prep_scatter, dim3(nblk), dim3(256), 0, st, idx, logp, r0, rows,
+                       int(p.K), int(p.V), int(p.nVt), ws.at<int>(p.off_counts),
+                       ws.at<int>(p.off_offsets), ws.at<uint2>(p.off_recs));
+  });
+}
+
+void launch_reset(const Plan& p, const Ws& ws, hipStream_t st) {
+  hipLaunchKernelGGL(k_fill_i32, dim3(cdiv(p.nb, 256)), dim3(256), 0, st, ws.at<int>(p.off_counts),
+                     int64_t(p.nb), 0);
+  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, st, ws.at<int>(p.off_flag), int64_t(64), 0);
+}
+
+template <bool BF16>
+int run_fwd(const Plan& p, const void* H, const void* W, const int32_t* idx, const float* logp,
+            float* loss_tok, float* lse, float* loss_sum, void* workspace, hipStream_t st) {
+  Ws ws{static_cast<char*>(workspace), p};
+  float* loss = loss_tok ? loss_tok : ws.at<float>(p.off_loss);
+  if (p.N > 0) {
+    launch_reset(p, ws, st);
+    const int64_t row_bytes = p.d * p.es;
+    for (int64_t r0 = 0; r0 < p.N; r0 += p.C) {
+      const int rows = int(p.N - r0 < p.C ? p.N - r0 : p.C);
+      launch_prep(p, ws, idx, logp, r0, rows, st);
+      FwdArgs a;
+      a.H = RowOp{static_cast<const char*>(H) + r0 * row_bytes, row_bytes, rows, int(row_bytes)};
+      a.W = RowOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
+      a.kt = int(p.kt_d);
+      a.tiles_m = int(cdiv(rows, kBM));
+      a.tiles_n = int(p.nVt);
+      a.rows = rows;
+      a.V = int(p.V);
+      a.K = int(p.K);
+      a.nVt = int(p.nVt);
+      a.offsets = ws.at<int>(p.off_offsets);
+      a.recs = ws.at<uint2>(p.off_recs);
+      a.zhit = ws.at<float>(p.off_zhit);
+      a.part = ws.at<float2>(p.off_part);
+      timed(KD_KERNEL_FWD_LOGITS, st, [&] {
+        hipLaunchKernelGGL(k_fwd_logits<BF16>, dim3(a.tiles_m * a.tiles_n), dim3(kThreads), 0, st,
+                           a);
+      });
+      timed(KD_KERNEL_OTHER, st, [&] {
+        hipLaunchKernelGGL(k_fwd_combine, dim3(cdiv(rows, 4)), dim3(256), 0, st, a.part, a.nVt,
+                           a.zhit, idx, logp, r0, rows, a.K, a.V, lse, loss);
+      });
+    }
+  }
+  hipLaunchKernelGGL(k_sum_fixed, dim3(1), dim3(1024), 0, st, loss, p.N, loss_sum);
+  return launch_status();
+}
+
+template <bool BF16>
+int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, const float* logp,
+            const float* lse, const float* grad, void* dH, float* dW, int accumulate,
+            void* workspace, hipStream_t st) {
+  Ws ws{static_cast<char*>(workspace), p};
+  if (p.N == 0) {
+    if (dW && !accumulate)
+      hipLaunchKernelGGL(k_fill_f32, dim3(1024), dim3(256), 0, st, dW, p.V * p.d, 0.f);
+    return launch_status();
+  }
+  launch_reset(p, ws, st);
+  const int64_t row_bytes = p.d * p.es;
+  const int kBKe = kLdsRow / p.es;
+  for (int64_t r0 = 0; r0 < p.N; r0 += p.C) {
+    const int rows = int(p.N - r0 < p.C ? p.N - r0 : p.C);
+    launch_prep(p, ws, idx, logp, r0, rows, st);
+    const char* Hc = static_cast<const char*>(H) + r0 * row_bytes;
+    const int tiles_m = int(cdiv(rows, kBM));
+
+    DlArgs a;
+    a.H = RowOp{Hc, row_bytes, rows, int(row_bytes)};
+    a.W = RowOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
+    a.kt = int(p.kt_d);
+    a.tiles_m = tiles_m;
+    a.tiles_n = int(p.nVt);
+    a.rows = rows;
+    a.V = int(p.V);
+    a.nVt = int(p.nVt);
+    a.offsets = ws.at<int>(p.off_offsets);
+    a.recs = ws.at<uint2>(p.off_recs);
+    a.lse = lse + r0;
+    a.rowS = ws.at<float>(p.off_rowS);
+    a.grad = grad;
+    a.dl = ws.at<char>(p.off_dl);
+    a.ld_dl = p.V_pad;
+    timed(KD_KERNEL_BWD_DLOGITS, st, [&] {
+      hipLaunchKernelGGL(k_bwd_dlogits<BF16>, dim3(a.tiles_m * a.tiles_n), dim3(kThreads), 0, st,
+                         a);
+    });
+
+    const int64_t dl_ld_bytes = p.V_pad * p.es;
+    if (dH) {
+      DhArgs h;
+      h.dl = RowOp{ws.at<char>(p.off_dl), dl_ld_bytes, rows, int(dl_ld_bytes)};
+      h.W = ColOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
+      h.tiles_m = tiles_m;
+      h.tiles_n = int(cdiv(p.d, kBN));
+      h.splits = p.dh_splits;
+      h.kt_total = int(p.kt_v);
+      h.rows = rows;
+      h.d = int(p.d);
+      h.dH = static_cast<char*>(dH) + r0 * row_bytes;
+      h.part = p.dh_splits > 1 ? ws.at<float>(p.off_dhpart) : nullptr;
+      h.part_stride = p.C_pad * p.d;
+      timed(KD_KERNEL_BWD_DH, st, [&] {
+        hipLaunchKernelGGL(k_bwd_dh<BF16>, dim3(h.tiles_m * h.tiles_n * h.splits), dim3(kThreads),
+                           0, st, h);
+      });
+      if (p.dh_splits > 1) {
+        const int64_t n = int64_t(rows) * p.d;
+        const int nb = int(cdiv(n, 256) < 4096 ? cdiv(n, 256) : 4096);
+        timed(KD_KERNEL_OTHER, st, [&] {
+          hipLaunchKernelGGL(k_bwd_dh_reduce<BF16>, dim3(nb), dim3(256), 0, st, h.part, h.splits,
+                             h.part_stride, n, h.dH);
+        });
+      }
+    }
+    if (dW) {
+      DwArgs w;
+      w.dl = ColOp{ws.at<char>(p.off_dl), dl_ld_bytes, rows, int(dl_ld_bytes)};
+      w.H = ColOp{Hc, row_bytes, rows, int(row_bytes)};
+      w.tiles_m = int(cdiv(p.V, kBM));
+      w.tiles_n = int(cdiv(p.d, kBN));
+      w.kt = int(cdiv(rows, kBKe));
+      w.V = int(p.V);
+      w.d = int(p.d);
+      w.dW = dW;
+      w.beta = (accumulate || r0 > 0) ? 1 : 0;
+      timed(KD_KERNEL_BWD_DW, st, [&] {
+        hipLaunchKernelGGL(k_bwd_dw<BF16>, dim3(w.tiles_m * w.tiles_n), dim3(kThreads), 0, st, w);
+      });
+    }
+  }
+  return launch_status();
+}
+
+inline bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+}  // namespace
+}  // namespace kd
+
+// --------------------------------------------------------------------------
+// C entry points
+// --------------------------------------------------------------------------
+extern "C" {
+
+const char* kd_status_str(int status) {
+  switch (status) {
+    case KD_OK: return "KD_OK";
+    case KD_ERR_INVALID_ARG: return "KD_ERR_INVALID_ARG";
+    case KD_ERR_UNSUPPORTED: return "KD_ERR_UNSUPPORTED";
+    case KD_ERR_WORKSPACE: return "KD_ERR_WORKSPACE";
+    case KD_ERR_HIP: return "KD_ERR_HIP";
+    default: return "KD_UNKNOWN_STATUS";
+  }
+}
+
+size_t kd_fused_kl_workspace_bytes(int pass, int64_t N, int64_t d, int64_t V, int64_t K,
+                                   int64_t chunk, int dtype) {
+  kd::Plan p;
+  if (kd::make_plan(pass, N, d, V, K, chunk, dtype, &p) != KD_OK) return 0;
+  return p.total;
+}
+
+int kd_fused_kl_fwd(const void* H, const void* W, int dtype, const int32_t* topk_idx,
+                    const float* topk_logp, int64_t N, int64_t d, int64_t V, int64_t K,
+                    int64_t chunk, float* loss_tok, float* lse, float* loss_sum, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  kd::Plan p;
+  const int st = kd::make_plan(KD_PASS_FWD, N, d, V, K, chunk, dtype, &p);
+  if (st != KD_OK) return st;
+  if (loss_sum == nullptr || !kd::aligned(loss_sum, 4)) return KD_ERR_INVALID_ARG;
+  if (N > 0) {
+    if (!H || !W || !topk_idx || !topk_logp || !lse) return KD_ERR_INVALID_ARG;
+    if (!kd::aligned(H, 16) || !kd::aligned(W, 16) || !kd::aligned(topk_idx, 4) ||
+        !kd::aligned(topk_logp, 4) || !kd::aligned(lse, 4) ||
+        (loss_tok && !kd::aligned(loss_tok, 4)))
+      return KD_ERR_INVALID_ARG;
+  }
+  if (!workspace || !kd::aligned(workspace, 256) || workspace_bytes < p.total)
+    return KD_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return dtype == KD_BF16
+             ? kd::run_fwd<true>(p, H, W, topk_idx, topk_logp, loss_tok, lse, loss_sum, workspace, s)
+             : kd::run_fwd<false>(p, H, W, topk_idx, topk_logp, loss_tok, lse, loss_sum, workspace, s);
+}
+
+int kd_fused_kl_bwd(const void* H, const void* W, int dtype, const int32_t* topk_idx,
+                    const float* topk_logp, const float* lse, int64_t N, int64_t d, int64_t V,
+                    int64_t K, int64_t chunk, const float* grad_loss, void* dH, float* dW,
+                    int dW_accumulate, void* workspace, size_t workspace_bytes, void* stream) {
+  kd::Plan p;
+  const int st = kd::make_plan(KD_PASS_BWD, N, d, V, K, chunk, dtype, &p);
+  if (st != KD_OK) return st;
+  if (dW_accumulate != 0 && dW_accumulate != 1) return KD_ERR_INVALID_ARG;
+  if (dW && !kd::aligned(dW, 16)) return KD_ERR_INVALID_ARG;
+  if (N > 0) {
+    if (!H || !W || !topk_idx || !topk_logp || !lse || !grad_loss) return KD_ERR_INVALID_ARG;
+    if (!kd::aligned(H, 16) || !kd::aligned(W, 16) || !kd::aligned(topk_idx, 4) ||
+        !kd::aligned(topk_logp, 4) || !kd::aligned(lse, 4) || !kd::aligned(grad_loss, 4) ||
+        (dH && !kd::aligned(dH, 16)))
+      return KD_ERR_INVALID_ARG;
+  }
+  if (!workspace || !kd::aligned(workspace, 256) || workspace_bytes < p.total)
+    return KD_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return dtype == KD_BF16 ? kd::run_bwd<true>(p, H, W, topk_idx, topk_logp, lse, grad_loss, dH, dW,
+                                              dW_accumulate, workspace, s)
+                          : kd::run_bwd<false>(p, H, W, topk_idx, topk_logp, lse, grad_loss, dH, dW,
+                                               dW_accumulate, workspace, s);
+}
+
+int kd_timing_enable(int enable) {
+  if (enable != 0 && enable != 1) return KD_ERR_INVALID_ARG;
+  kd::g_timing = enable == 1;
+  return KD_OK;
+}
+
+int kd_timing_read(double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return KD_ERR_INVALID_ARG;
+  for (int c = 0; c < KD_KERNEL_CLASSES; ++c) {
+    total_ms[c] = 0.0;
+    launches[c] = 0;
+  }
+  int st = KD_OK;
+  for (const kd::TimingRec& r : kd::g_timing_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      st = KD_ERR_HIP;
+      continue;
+    }
+    total_ms[r.cls] += ms;
+    launches[r.cls] += 1;
+  }
+  kd::g_timing_recs.clear();
+  kd::g_events_used = 0;
+  return st;
+}
+
+int kd_cast_f32_to_bf16(const float* src, void* dst, int64_t n, void* stream) {
+  if (n < 0) return KD_ERR_INVALID_ARG;
+  if (n == 0) return KD_OK;
+  if (!src || !dst || !kd::aligned(src, 4) || !kd::aligned(dst, 2)) return KD_ERR_INVALID_ARG;
+  const char* s0 = reinterpret_cast<const char*>(src);
+  const char* d0 = static_cast<const char*>(dst);
+  if (d0 < s0 + 4 * n && s0 < d0 + 2 * n) return KD_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(kd::k_cast_f32_bf16, dim3(4096), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     src, static_cast<__bf16*>(dst), n);
+  return kd::launch_status();
+}
+
+}  // extern "C"

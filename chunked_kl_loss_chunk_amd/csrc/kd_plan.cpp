@@ -1,0 +1,85 @@
+// kd_plan.cpp — validation and workspace layout (host only, no HIP calls).
+#include "kd_plan.h"
+
+#include "kd_fused_kl.h"
+
+namespace kd {
+namespace {
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, int dtype,
+              Plan* p) {
+  if (p == nullptr) return KD_ERR_INVALID_ARG;
+  if (pass != KD_PASS_FWD && pass != KD_PASS_BWD) return KD_ERR_INVALID_ARG;
+  if (dtype != KD_F32 && dtype != KD_BF16) return KD_ERR_INVALID_ARG;
+  if (N < 0 || d <= 0 || V <= 0 || K <= 0 || chunk <= 0) return KD_ERR_INVALID_ARG;
+  if (K > V) return KD_ERR_INVALID_ARG;
+  const int es = dtype == KD_BF16 ? 2 : 4;
+  // 16-byte rows: every H, W and dH row starts on a 16-byte boundary.
+  if ((d * es) % 16 != 0) return KD_ERR_INVALID_ARG;
+  if (K > kMaxK) return KD_ERR_UNSUPPORTED;
+  // 32-bit limits inside the kernels (row counts, tile counts, per-chunk
+  // entry counts); global byte offsets are computed in 64 bits.
+  if (N > (int64_t(1) << 31) - 1 || V > (int64_t(1) << 28) || d > (int64_t(1) << 20))
+    return KD_ERR_UNSUPPORTED;
+
+  Plan q{};
+  q.N = N;
+  q.d = d;
+  q.V = V;
+  q.K = K;
+  q.chunk = chunk;
+  q.dtype = dtype;
+  q.es = es;
+  q.C = chunk < (N > 0 ? N : 1) ? chunk : (N > 0 ? N : 1);
+  q.C_pad = cdiv(q.C, kTileM) * kTileM;
+  q.V_pad = cdiv(V, kTileN) * kTileN;
+  q.nVt = q.V_pad / kTileN;
+  q.nMt = q.C_pad / kTileM;
+  q.nb = q.nMt * q.nVt;
+  q.kt_d = cdiv(d * es, kStageBytes);
+  q.kt_v = cdiv(q.V_pad * es, kStageBytes);
+  if (q.C * K > (int64_t(1) << 30) || q.nb > (int64_t(1) << 30)) return KD_ERR_UNSUPPORTED;
+
+  // dH = dlogits · W has a short output (C × d) and a long contraction (V):
+  // split the contraction so that enough workgroups exist to fill the chip.
+  const int64_t tiles_mn = q.nMt * cdiv(d, kTileN);
+  int64_t splits = cdiv(kDhTargetTiles, tiles_mn);
+  if (splits > kMaxDhSplits) splits = kMaxDhSplits;
+  if (splits > q.kt_v) splits = q.kt_v;
+  if (splits < 1) splits = 1;
+  q.dh_splits = static_cast<int>(splits);
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  q.off_flag = take(256);
+  q.off_counts = take(sizeof(int32_t) * size_t(q.nb));
+  q.off_offsets = take(sizeof(int32_t) * size_t(q.nb + 1));
+  q.off_recs = take(8 * size_t(q.C * K));
+  q.off_rowS = take(sizeof(float) * size_t(q.C_pad));
+  if (pass == KD_PASS_FWD) {
+    q.off_zhit = take(sizeof(float) * size_t(q.C * K));
+    q.off_part = take(8 * size_t(q.C_pad * q.nVt));
+    q.off_loss = take(sizeof(float) * size_t(N > 0 ? N : 1));
+    q.off_dl = q.off_dhpart = 0;
+  } else {
+    q.off_zhit = q.off_part = q.off_loss = 0;
+    q.off_dl = take(size_t(es) * size_t(q.C_pad) * size_t(q.V_pad));
+    q.off_dhpart = q.dh_splits > 1 ? take(sizeof(float) * size_t(q.dh_splits) * size_t(q.C_pad) *
+                                          size_t(d))
+                                    : 0;
+  }
+  q.total = off;
+  *p = q;
+  return KD_OK;
+}
+
+}  // namespace kd

@@ -1,0 +1,47 @@
+// kd_plan.h — argument validation and workspace layout of the fused, chunked
+// top-K KL loss. Pure C++: no HIP calls, so it runs (and is tested) on a host
+// without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kd {
+
+// Tile of the logit GEMM (rows of a chunk × vocabulary columns). The top-K
+// hit lists are bucketed by this tile, so the plan fixes it.
+constexpr int kTileM = 128;
+constexpr int kTileN = 128;
+// Bytes of the contraction dimension staged per LDS row and pipeline stage.
+constexpr int kStageBytes = 128;
+// Packed hit record: row-in-tile (8 bits), column-in-tile (10 bits), k (14 bits).
+constexpr int64_t kMaxK = (1 << 14) - 1;
+// Upper bound on the dH split-K factor.
+constexpr int kMaxDhSplits = 32;
+// Target number of dH workgroups per chunk (a few waves of the 256 CUs).
+constexpr int kDhTargetTiles = 1024;
+
+struct Plan {
+  int64_t N, d, V, K, chunk;
+  int dtype;      // 0 = f32, 1 = bf16
+  int es;         // element size in bytes
+  int64_t C;      // rows per chunk actually used: min(chunk, max(N, 1))
+  int64_t C_pad;  // C rounded up to kTileM
+  int64_t V_pad;  // V rounded up to kTileN
+  int64_t nVt;    // vocabulary tiles
+  int64_t nMt;    // row tiles per chunk
+  int64_t nb;     // hit buckets per chunk = nMt * nVt
+  int64_t kt_d;   // stages along d   (d * es / kStageBytes, rounded up)
+  int64_t kt_v;   // stages along V_pad
+  int dh_splits;  // split-K factor of the dH contraction
+  // byte offsets inside the workspace (all 256-byte aligned)
+  size_t off_counts, off_offsets, off_recs, off_rowS, off_zhit, off_part, off_loss, off_flag;
+  size_t off_dl, off_dhpart;
+  size_t total;
+};
+
+// Fills *p for the given pass (0 forward, 1 backward). Returns a kd_status.
+int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, int dtype,
+              Plan* p);
+
+}  // namespace kd

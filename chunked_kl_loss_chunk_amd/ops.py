@@ -1,0 +1,157 @@
+"""Python face of the fused, chunked top-K KL loss (thin layer over the C ABI).
+
+PyTorch supplies device memory and the current stream; every step of the loss
+runs in the HIP kernels of libkdkl.so. Functions here check shapes and dtypes,
+allocate outputs and the workspace with torch, and call the library.
+
+    loss = fused_kl(H, W, topk_idx, topk_logp, chunk=1024)   # autograd-aware
+    loss.backward()                                           # dH, dW via HIP
+
+Source: the fused, chunked KL loss of "Hugging Face：让知识蒸馏廉价到可大规模运行"
+(section 为什么蒸馏恢复代价高昂, "Fused chunked KL" paragraph), fed by the
+offline top-K teacher cache of the same page (section 离线蒸馏).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.KD_F32, torch.bfloat16: _lib.KD_BF16}
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt not in _DT:
+        raise TypeError(f"H and W must be float32 or bfloat16, got {dt}")
+    return _DT[dt]
+
+
+def workspace_bytes(pass_: int, N: int, d: int, V: int, K: int, chunk: int, dt: torch.dtype) -> int:
+    n = _lib.lib().kd_fused_kl_workspace_bytes(int(pass_), N, d, V, K, chunk, dtype_code(dt))
+    if n == 0:
+        raise ValueError(f"invalid sizes N={N} d={d} V={V} K={K} chunk={chunk} dtype={dt}")
+    return int(n)
+
+
+def _check_inputs(H, W, idx, logp):
+    if not (H.is_cuda and W.is_cuda and idx.is_cuda and logp.is_cuda):
+        raise ValueError("all inputs must be on the GPU")
+    if H.dim() != 2 or W.dim() != 2 or idx.dim() != 2 or logp.dim() != 2:
+        raise ValueError("H [N,d], W [V,d], idx [N,K], logp [N,K] expected")
+    N, d = H.shape
+    V, d2 = W.shape
+    if d2 != d or idx.shape != logp.shape or idx.shape[0] != N:
+        raise ValueError(f"shape mismatch: H {tuple(H.shape)} W {tuple(W.shape)} "
+                         f"idx {tuple(idx.shape)} logp {tuple(logp.shape)}")
+    if H.dtype != W.dtype:
+        raise TypeError("H and W must share a dtype")
+    if idx.dtype != torch.int32 or logp.dtype != torch.float32:
+        raise TypeError("topk_idx must be int32 and topk_logp float32")
+    for t in (H, W, idx, logp):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    return N, d, V, idx.shape[1]
+
+
+def kl_forward(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, logp: torch.Tensor,
+               chunk: int, want_loss_tok: bool = True
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor], torch.Tensor]:
+    """Returns (loss_sum [1] fp32, loss_tok [N] fp32 or None, lse [N] fp32)."""
+    N, d, V, K = _check_inputs(H, W, idx, logp)
+    dev = H.device
+    dt = dtype_code(H.dtype)
+    ws_n = workspace_bytes(_lib.KD_PASS_FWD, N, d, V, K, chunk, H.dtype)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    loss_sum = torch.empty(1, dtype=torch.float32, device=dev)
+    loss_tok = torch.empty(N, dtype=torch.float32, device=dev) if want_loss_tok else None
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    st = _lib.lib().kd_fused_kl_fwd(_p(H), _p(W), dt, _p(idx), _p(logp), N, d, V, K, chunk,
+                                     _p(loss_tok), _p(lse), _p(loss_sum), _p(ws), ws_n, _stream(dev))
+    _lib.check("kd_fused_kl_fwd", st)
+    return loss_sum, loss_tok, lse
+
+
+def kl_backward(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, logp: torch.Tensor,
+                lse: torch.Tensor, grad: torch.Tensor, chunk: int, need_dH: bool = True,
+                need_dW: bool = True, dW_out: Optional[torch.Tensor] = None,
+                accumulate: bool = False) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """Returns (dH [N,d] in H's dtype or None, dW [V,d] fp32 or None).
+
+    ``grad`` is a 1-element fp32 device tensor: ∂objective/∂loss_sum.
+    ``dW_out`` (fp32 [V,d]) is written, or added to when ``accumulate``.
+    """
+    N, d, V, K = _check_inputs(H, W, idx, logp)
+    dev = H.device
+    if lse.shape != (N,) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [N] tensor from kl_forward")
+    grad = grad.reshape(1).to(device=dev, dtype=torch.float32).contiguous()
+    dt = dtype_code(H.dtype)
+    ws_n = workspace_bytes(_lib.KD_PASS_BWD, N, d, V, K, chunk, H.dtype)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    dH = torch.empty((N, d), dtype=H.dtype, device=dev) if need_dH else None
+    dW = None
+    if need_dW:
+        if dW_out is not None:
+            if dW_out.shape != (V, d) or dW_out.dtype != torch.float32 or not dW_out.is_contiguous():
+                raise ValueError("dW_out must be a contiguous fp32 [V,d] tensor")
+            dW = dW_out
+        else:
+            dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+            accumulate = False
+    st = _lib.lib().kd_fused_kl_bwd(_p(H), _p(W), dt, _p(idx), _p(logp), _p(lse), N, d, V, K, chunk,
+                                     _p(grad), _p(dH), _p(dW), 1 if accumulate else 0, _p(ws), ws_n,
+                                     _stream(dev))
+    _lib.check("kd_fused_kl_bwd", st)
+    return dH, dW
+
+
+def cast_f32_to_bf16(x: torch.Tensor) -> torch.Tensor:
+    """fp32 -> bf16 (round to nearest even) in a HIP kernel."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("expected a contiguous fp32 GPU tensor")
+    out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    st = _lib.lib().kd_cast_f32_to_bf16(_p(x), _p(out), x.numel(), _stream(x.device))
+    _lib.check("kd_cast_f32_to_bf16", st)
+    return out
+
+
+class FusedTopKKL(torch.autograd.Function):
+    """Σ over positions of KL(teacher top-K ‖ student softmax(H Wᵀ)).
+
+    Saves only lse [N] between the passes; the backward pass recomputes the
+    logits chunk by chunk.
+    """
+
+    @staticmethod
+    def forward(ctx, H, W, idx, logp, chunk):
+        loss_sum, _, lse = kl_forward(H, W, idx, logp, chunk, want_loss_tok=False)
+        ctx.save_for_backward(H, W, idx, logp, lse)
+        ctx.chunk = chunk
+        return loss_sum.reshape(())
+
+    @staticmethod
+    def backward(ctx, grad):
+        H, W, idx, logp, lse = ctx.saved_tensors
+        need_dH, need_dW = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        dH, dW = kl_backward(H, W, idx, logp, lse, grad, ctx.chunk, need_dH=need_dH,
+                             need_dW=need_dW)
+        if dW is not None and W.dtype == torch.bfloat16:
+            dW = cast_f32_to_bf16(dW)
+        return dH, dW, None, None, None
+
+
+def fused_kl(H: torch.Tensor, W: torch.Tensor, topk_idx: torch.Tensor, topk_logp: torch.Tensor,
+             chunk: int = 1024) -> torch.Tensor:
+    """Summed top-K KL distillation loss; differentiable in H and W."""
+    return FusedTopKKL.apply(H, W, topk_idx, topk_logp, int(chunk))

@@ -1,0 +1,163 @@
+/*
+ * kd_fused_kl.h — C ABI of the fused, chunked top-K KL distillation loss on
+ * AMD MI355X (gfx950).
+ *
+ * Source pages (cited by title and section):
+ *  [P1] "Distilação de LLMs mais barata: top-K offline e KL fundida cortam
+ *       VRAM em até 15x" (imasters.com.br)
+ *  [P3] "Destilación de LLMs: Multiverse Computing reduce memoria 15× con
+ *       1 GPU" (ecosistemastartup.com)
+ *  [P4] "Hugging Face：让知识蒸馏廉价到可大规模运行" (feinterview.poetries.top)
+ *  [P5] "Chunkovaná KL strata umožnila destilovať LLM s 32-tisícovým
+ *       kontextom na jednom H200" (aifeed.sk)
+ *
+ * What the library computes. Student hidden states H[N,d] are projected
+ * through the output head W[V,d] one chunk of positions at a time; the logits
+ * of a chunk are folded into an accumulated loss and discarded, and the
+ * backward pass recomputes them instead of storing them ([P1] "As duas
+ * mudanças"; [P4] 为什么蒸馏恢复代价高昂, "Fused chunked KL" paragraph). The
+ * teacher side is an offline top-K cache: for each position, K token ids and
+ * their log-probabilities, not renormalised ([P4] 离线蒸馏; [P5] "Čo dopĺňajú
+ * podrobnejšie experimenty"). With z = H Wᵀ, lse_r = log Σ_j exp z_rj over the
+ * full vocabulary, p_rk = exp(logp_rk) and S_r = Σ_k p_rk:
+ *
+ *   loss_tok[r] = Σ_k p_rk (logp_rk − z_r,idx_rk + lse_r)   (forward KL)
+ *   loss_sum    = Σ_r loss_tok[r]                          (sum over rows)
+ *   dlogits_rj  = g (S_r exp(z_rj − lse_r) − Σ_k p_rk [j = idx_rk])
+ *   dH = dlogits W,  dW = dlogitsᵀ H
+ *
+ * which is the dense KL of the pages' correctness baseline rewritten so that
+ * no N×V grid exists ([P4], the three variants are mathematically
+ * equivalent). Chunk size is the caller's memory/speed knob ([P3]
+ * "Implementación práctica").
+ *
+ * Conventions for every entry point:
+ *  - All array arguments are DEVICE pointers owned by the caller, row-major
+ *    and contiguous. H, W and dH rows must start on 16-byte boundaries
+ *    (d*sizeof(element) % 16 == 0 and 16-byte aligned base pointers).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously on it; the library never allocates,
+ *    frees, synchronises or prints.
+ *  - `workspace` is a caller-owned device buffer of at least
+ *    kd_fused_kl_workspace_bytes(...) bytes, 256-byte aligned; its contents
+ *    on entry are irrelevant and on exit unspecified.
+ *  - Invalid arguments are reported by the return value BEFORE anything is
+ *    enqueued. A failed launch returns KD_ERR_HIP.
+ *  - Preconditions not checked on the host: teacher ids are distinct within
+ *    a row; logp values are <= 0 and finite or −inf (−inf means p = 0 and the
+ *    entry contributes nothing). Ids outside [0, V) are skipped by the
+ *    kernels (never dereferenced) and count as p = 0.
+ *  - Results are deterministic: every reduction runs in a fixed order.
+ *  - Calls that share one workspace must not overlap.
+ */
+#ifndef KD_FUSED_KL_H
+#define KD_FUSED_KL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+typedef enum {
+  KD_OK = 0,
+  KD_ERR_INVALID_ARG = 1, /* a size, pointer, alignment or flag is invalid */
+  KD_ERR_UNSUPPORTED = 2, /* well-formed but outside what the kernels take  */
+  KD_ERR_WORKSPACE = 3,   /* workspace NULL, misaligned or too small        */
+  KD_ERR_HIP = 4          /* a kernel launch failed                         */
+} kd_status;
+
+/* Element type of H, W and dH. */
+typedef enum { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
+
+/* Which pass a workspace query is for. */
+typedef enum { KD_PASS_FWD = 0, KD_PASS_BWD = 1 } kd_pass;
+
+/* Human-readable name of a status code; never NULL. */
+const char* kd_status_str(int status);
+
+/*
+ * Bytes of workspace kd_fused_kl_fwd (pass = KD_PASS_FWD) or kd_fused_kl_bwd
+ * (pass = KD_PASS_BWD) needs for these sizes. Returns 0 if the sizes are
+ * invalid (the same checks the entry points make). The backward workspace
+ * holds one chunk's dlogits, chunk × V elements of `dtype` (padded to the
+ * kernel tile), so it grows with the chunk, never with N × V.
+ */
+size_t kd_fused_kl_workspace_bytes(int pass, int64_t N, int64_t d, int64_t V, int64_t K,
+                                   int64_t chunk, int dtype);
+
+/*
+ * Forward: loss of every position, the saved log-normaliser, and their sum.
+ *
+ *  H         [N, d] of `dtype` — student hidden states.
+ *  W         [V, d] of `dtype` — output head (student projection).
+ *  topk_idx  [N, K] int32 — cached teacher token ids.
+ *  topk_logp [N, K] float32 — cached teacher log-probabilities.
+ *  N, d, V, K, chunk — sizes; 1 <= K <= V, chunk >= 1, N >= 0.
+ *  loss_tok  [N] float32 or NULL — per-position loss.
+ *  lse       [N] float32 — log Σ_j exp z_rj, saved for the backward pass.
+ *  loss_sum  [1] float32 — Σ_r loss_tok[r], reduced in a fixed order.
+ *
+ * N = 0 writes loss_sum = 0. Rows are processed `chunk` at a time.
+ */
+int kd_fused_kl_fwd(const void* H, const void* W, int dtype, const int32_t* topk_idx,
+                    const float* topk_logp, int64_t N, int64_t d, int64_t V, int64_t K,
+                    int64_t chunk, float* loss_tok, float* lse, float* loss_sum, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * Backward: recomputes each chunk's logits from H and W (they are never
+ * stored between passes), forms dlogits in registers, writes them once for
+ * the chunk, and contracts them into dH and dW.
+ *
+ *  H, W, topk_idx, topk_logp, N, d, V, K, chunk — as in the forward pass.
+ *  lse        [N] float32 — the forward pass's output for the same inputs.
+ *  grad_loss  [1] float32, DEVICE pointer — g = ∂objective/∂loss_sum (a
+ *             mean over tokens is g = 1/N); read by the kernels, so no host
+ *             synchronisation is needed.
+ *  dH         [N, d] of `dtype`, or NULL to skip — overwritten.
+ *  dW         [V, d] float32, or NULL to skip — overwritten when
+ *             dW_accumulate == 0, added to when dW_accumulate == 1.
+ */
+int kd_fused_kl_bwd(const void* H, const void* W, int dtype, const int32_t* topk_idx,
+                    const float* topk_logp, const float* lse, int64_t N, int64_t d, int64_t V,
+                    int64_t K, int64_t chunk, const float* grad_loss, void* dH, float* dW,
+                    int dW_accumulate, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Element-wise float32 -> bfloat16 (round to nearest even) of n values, for
+ * callers that keep W in bf16 and want dW in W's dtype. Device pointers;
+ * src and dst must not overlap.
+ */
+int kd_cast_f32_to_bf16(const float* src, void* dst, int64_t n, void* stream);
+
+/*
+ * Kernel timing, for benchmarks. Not part of the loss.
+ *
+ * kd_timing_enable(1) makes every later fwd/bwd call bracket its kernel
+ * launches with HIP events on the caller's stream (kd_timing_enable(0) stops
+ * it). kd_timing_read waits for the recorded events, writes per kernel class
+ * the summed milliseconds (total_ms[KD_KERNEL_CLASSES]) and launch counts
+ * (launches[KD_KERNEL_CLASSES]), and clears the record. A "launch" of
+ * KD_KERNEL_PREP is the three prep kernels of one chunk. Not thread-safe;
+ * this is the one entry point that synchronises (with its own events).
+ */
+enum {
+  KD_KERNEL_PREP = 0,         /* bucket the chunk's top-K entries             */
+  KD_KERNEL_FWD_LOGITS = 1,   /* fused logit tile + logsumexp partials        */
+  KD_KERNEL_BWD_DLOGITS = 2,  /* recomputed logit tile -> dlogits             */
+  KD_KERNEL_BWD_DH = 3,       /* dH = dlogits W                               */
+  KD_KERNEL_BWD_DW = 4,       /* dW (+)= dlogitsᵀ H                           */
+  KD_KERNEL_OTHER = 5,        /* combine, split reduce                        */
+  KD_KERNEL_CLASSES = 6
+};
+int kd_timing_enable(int enable);
+int kd_timing_read(double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KD_FUSED_KL_H */

@@ -1,0 +1,147 @@
+"""The C ABI on a host without a GPU: the library loads, exports every symbol
+the header declares, sizes its workspace, and rejects every invalid argument
+before anything is enqueued. Every call below has at least one invalid
+argument, so no kernel is ever launched and no pointer is dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from chunked_kl_loss_chunk_amd import _build, _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kd_fused_kl.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_build.LIB_PATH):
+        _build.build()
+    return _lib.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_all_exported(L):
+    names = _declared_functions()
+    assert "kd_fused_kl_fwd" in names and "kd_fused_kl_bwd" in names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in the header but not exported"
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings(L):
+    assert _lib.status_str(0) == "KD_OK"
+    assert _lib.status_str(3) == "KD_ERR_WORKSPACE"
+    assert _lib.status_str(4) == "KD_ERR_HIP"
+    assert _lib.status_str(99) == "KD_UNKNOWN_STATUS"
+
+
+def _ws(L, pass_, N, d, V, K, C, dt):
+    return L.kd_fused_kl_workspace_bytes(pass_, N, d, V, K, C, dt)
+
+
+def test_workspace_size_rules(L):
+    f, b = _lib.KD_PASS_FWD, _lib.KD_PASS_BWD
+    bf, f32 = _lib.KD_BF16, _lib.KD_F32
+    # invalid sizes -> 0
+    assert _ws(L, f, -1, 64, 1000, 8, 32, f32) == 0
+    assert _ws(L, f, 128, 0, 1000, 8, 32, f32) == 0
+    assert _ws(L, f, 128, 64, 1000, 1001, 32, f32) == 0  # K > V
+    assert _ws(L, f, 128, 64, 1000, 0, 32, f32) == 0
+    assert _ws(L, f, 128, 64, 1000, 8, 0, f32) == 0
+    assert _ws(L, f, 128, 63, 1000, 8, 32, f32) == 0  # 63*4 bytes is not a multiple of 16
+    assert _ws(L, f, 128, 68, 1000, 8, 32, bf) == 0   # 68*2 bytes is not a multiple of 16
+    assert _ws(L, f, 128, 64, 1000, 8, 32, 7) == 0
+    assert _ws(L, 2, 128, 64, 1000, 8, 32, f32) == 0
+    assert _ws(L, f, 128, 64, 100000, 20000, 32, f32) == 0  # K beyond the record format
+    # valid
+    wf = _ws(L, f, 8192, 3072, 128256, 100, 1024, bf)
+    wb = _ws(L, b, 8192, 3072, 128256, 100, 1024, bf)
+    assert wf > 0 and wb > 0 and wf % 256 == 0 and wb % 256 == 0
+    # the backward holds one chunk's dlogits: at least C x V_pad bf16, and
+    # it does not grow with N once N exceeds the chunk
+    V_pad = (128256 + 127) // 128 * 128
+    assert wb >= 1024 * V_pad * 2
+    assert _ws(L, b, 262144, 3072, 128256, 100, 1024, bf) == wb
+    assert _ws(L, b, 8192, 3072, 128256, 100, 2048, bf) > wb
+    # the forward workspace is small and linear in N (a per-token buffer)
+    w1 = _ws(L, f, 32768, 3072, 128256, 100, 2048, bf)
+    w2 = _ws(L, f, 65536, 3072, 128256, 100, 2048, bf)
+    w4 = _ws(L, f, 131072, 3072, 128256, 100, 2048, bf)
+    assert 0 < w2 - w1 <= 4 * 32768 + 256 and abs((w4 - w2) - 2 * (w2 - w1)) <= 512
+    # a chunk larger than N is clamped to N
+    assert _ws(L, b, 100, 64, 1000, 8, 4096, f32) == _ws(L, b, 100, 64, 1000, 8, 100, f32)
+
+
+FAKE = 0x100000  # 16-byte-aligned, never dereferenced (every call is rejected first)
+
+
+def _fwd(L, **kw):
+    a = dict(H=FAKE, W=FAKE, dt=_lib.KD_F32, idx=FAKE, logp=FAKE, N=128, d=64, V=1000, K=8, C=32,
+             loss_tok=FAKE, lse=FAKE, loss_sum=FAKE, ws=FAKE, ws_n=1 << 40, stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.kd_fused_kl_fwd(vp(a["H"]), vp(a["W"]), a["dt"], vp(a["idx"]), vp(a["logp"]), a["N"],
+                             a["d"], a["V"], a["K"], a["C"], vp(a["loss_tok"]), vp(a["lse"]),
+                             vp(a["loss_sum"]), vp(a["ws"]), a["ws_n"], a["stream"])
+
+
+def _bwd(L, **kw):
+    a = dict(H=FAKE, W=FAKE, dt=_lib.KD_F32, idx=FAKE, logp=FAKE, lse=FAKE, N=128, d=64, V=1000, K=8,
+             C=32, grad=FAKE, dH=FAKE, dW=FAKE, acc=0, ws=FAKE, ws_n=1 << 40, stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.kd_fused_kl_bwd(vp(a["H"]), vp(a["W"]), a["dt"], vp(a["idx"]), vp(a["logp"]),
+                             vp(a["lse"]), a["N"], a["d"], a["V"], a["K"], a["C"], vp(a["grad"]),
+                             vp(a["dH"]), vp(a["dW"]), a["acc"], vp(a["ws"]), a["ws_n"], a["stream"])
+
+
+INV, UNS, WSE = _lib.KD_ERR_INVALID_ARG, _lib.KD_ERR_UNSUPPORTED, _lib.KD_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(N=-1), INV), (dict(d=0), INV), (dict(V=0), INV), (dict(K=0), INV), (dict(K=1001), INV),
+    (dict(C=0), INV), (dict(C=-5), INV), (dict(dt=2), INV), (dict(d=63), INV),
+    (dict(K=20000, V=100000), UNS), (dict(V=(1 << 28) + 1), UNS),
+    (dict(H=None), INV), (dict(W=None), INV), (dict(idx=None), INV), (dict(logp=None), INV),
+    (dict(lse=None), INV), (dict(loss_sum=None), INV),
+    (dict(H=FAKE + 8), INV), (dict(W=FAKE + 4), INV), (dict(idx=FAKE + 2), INV),
+    (dict(loss_tok=FAKE + 1), INV), (dict(loss_sum=FAKE + 2), INV),
+    (dict(ws=None), WSE), (dict(ws=FAKE + 16), WSE), (dict(ws_n=1024), WSE),
+])
+def test_forward_rejects_invalid(L, kw, want):
+    assert _fwd(L, **kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(N=-1), INV), (dict(d=0), INV), (dict(K=1001), INV), (dict(C=0), INV), (dict(dt=5), INV),
+    (dict(acc=2), INV), (dict(acc=-1), INV),
+    (dict(H=None), INV), (dict(W=None), INV), (dict(lse=None), INV), (dict(grad=None), INV),
+    (dict(dH=FAKE + 8), INV), (dict(dW=FAKE + 4), INV), (dict(grad=FAKE + 2), INV),
+    (dict(ws=None), WSE), (dict(ws_n=4096), WSE),
+])
+def test_backward_rejects_invalid(L, kw, want):
+    assert _bwd(L, **kw) == want
+
+
+def test_cast_rejects_invalid(L):
+    vp = ctypes.c_void_p
+    assert L.kd_cast_f32_to_bf16(vp(FAKE), vp(FAKE), -1, None) == INV
+    assert L.kd_cast_f32_to_bf16(None, vp(FAKE), 10, None) == INV
+    assert L.kd_cast_f32_to_bf16(vp(FAKE), vp(FAKE + 8), 10, None) == INV  # overlap
+    assert L.kd_cast_f32_to_bf16(vp(FAKE), vp(FAKE), 0, None) == _lib.KD_OK  # nothing to do
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    from chunked_kl_loss_chunk_amd import ops
+    H = torch.zeros(4, 8)
+    with pytest.raises(ValueError):
+        ops.kl_forward(H, torch.zeros(10, 8), torch.zeros(4, 2, dtype=torch.int32),
+                       torch.zeros(4, 2), chunk=2)

@@ -1,0 +1,195 @@
+"""GPU parity: the HIP path against the fp64 CPU oracle on the same seeded inputs.
+
+Tolerances: fp32 workloads, relative 1e-4 on the loss and max-normalised 1e-4
+on dH and dW; bf16 workloads, relative 2e-3 on the loss and max-normalised
+2e-2 on dH and dW (max|X − X_ref| / max|X_ref|). lse is compared with the
+same tolerance as the loss.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": dict(loss=1e-4, grad=1e-4), "bf16": dict(loss=2e-3, grad=2e-2)}
+
+
+@pytest.fixture(scope="module")
+def kd():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import chunked_kl_loss_chunk_amd as kd
+    kd.lib()  # raises if the HIP library is missing: no fallback
+    return kd
+
+
+def _to_dev(H, W, idx, logp):
+    dev = torch.device("cuda:0")
+    return H.to(dev), W.to(dev), idx.to(dev), logp.to(dev)
+
+
+def run_hip(kd, H, W, idx, logp, chunk, grad=1.0, need_dH=True, need_dW=True):
+    Hd, Wd, id_, lp = _to_dev(H, W, idx, logp)
+    loss_sum, loss_tok, lse = kd.kl_forward(Hd, Wd, id_, lp, chunk)
+    g = torch.tensor([grad], dtype=torch.float32, device=Hd.device)
+    dH, dW = kd.kl_backward(Hd, Wd, id_, lp, lse, g, chunk, need_dH=need_dH, need_dW=need_dW)
+    torch.cuda.synchronize()
+    out = {"loss": float(loss_sum.item()), "loss_tok": loss_tok.double().cpu().numpy(),
+           "lse": lse.double().cpu().numpy()}
+    if dH is not None:
+        out["dH"] = dH.double().cpu().numpy()
+    if dW is not None:
+        out["dW"] = dW.double().cpu().numpy()
+    return out
+
+
+def max_norm_err(x, ref):
+    scale = np.abs(ref).max()
+    return float(np.abs(x - ref).max() / (scale if scale > 0 else 1.0))
+
+
+def rel_err(x, ref):
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.abs(x - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def assert_parity(got, ref, dtype, what=""):
+    t = TOL[dtype]
+    assert rel_err(got["loss"], ref["loss"]) < t["loss"], (what, got["loss"], ref["loss"])
+    assert rel_err(got["loss_tok"], ref["loss_tok"]) < t["loss"], what
+    assert rel_err(got["lse"], ref["lse"]) < t["loss"], what
+    if "dH" in got:
+        e = max_norm_err(got["dH"], ref["dH"])
+        assert e < t["grad"], (what, "dH", e)
+    if "dW" in got:
+        e = max_norm_err(got["dW"], ref["dW"])
+        assert e < t["grad"], (what, "dW", e)
+
+
+def _case(N, d, V, K, dtype, seed):
+    """A small seeded case in the workloads' recipe (H ~ N(0,1), W ~ N(0,1/d),
+    teacher head ~ N(0,4/d), top-K of the teacher softmax)."""
+    g = torch.Generator().manual_seed(seed)
+    H = torch.randn(N, d, generator=g)
+    W = torch.randn(V, d, generator=g) * d ** -0.5
+    if dtype == "bf16":
+        H, W = H.to(torch.bfloat16), W.to(torch.bfloat16)
+    Wt = torch.randn(V, d, generator=g) * 2.0 * d ** -0.5
+    idx, logp = workload.teacher_topk(H.float(), Wt, K)
+    return H.contiguous(), W.contiguous(), idx, logp
+
+
+def test_tiny_fp32_workload(kd):
+    cfg = workload.config(1)
+    H, W, idx, logp = workload.make_inputs(cfg)
+    got = run_hip(kd, H, W, idx, logp, cfg.chunk)
+    ref = oracle.fused_kl_reference(H, W, idx, logp)
+    assert_parity(got, ref, "f32", "cfg1")
+
+
+def test_small_bf16_workload(kd):
+    cfg = workload.config(2)
+    H, W, idx, logp = workload.make_inputs(cfg)
+    got = run_hip(kd, H, W, idx, logp, cfg.chunk)
+    ref = oracle.fused_kl_reference(H, W, idx, logp)
+    assert_parity(got, ref, "bf16", "cfg2")
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 32, 100, 128, 1000])
+def test_chunk_size_does_not_change_results(kd, chunk):
+    cfg = workload.config(1)
+    H, W, idx, logp = workload.make_inputs(cfg)
+    got = run_hip(kd, H, W, idx, logp, chunk)
+    ref = oracle.fused_kl_reference(H, W, idx, logp)
+    assert_parity(got, ref, "f32", f"chunk={chunk}")
+
+
+@pytest.mark.parametrize("N,d,V,K,dtype,chunk", [
+    (130, 64, 129, 5, "f32", 64),        # ragged rows and a one-column last vocab tile
+    (5, 16, 300, 3, "f32", 4),           # fewer rows than a tile, tiny d
+    (200, 200, 1000, 17, "bf16", 96),    # d not a multiple of the 64-element stage
+    (257, 72, 515, 1, "bf16", 128),      # K = 1
+    (64, 32, 40, 40, "f32", 16),         # K = V: the full teacher distribution
+    (300, 160, 2000, 100, "bf16", 256),  # K = 100 over a small vocabulary
+])
+def test_edge_shapes(kd, N, d, V, K, dtype, chunk):
+    H, W, idx, logp = _case(N, d, V, K, dtype, seed=N * 7 + V)
+    got = run_hip(kd, H, W, idx, logp, chunk, grad=0.37)
+    ref = oracle.fused_kl_reference(H, W, idx, logp, grad=0.37)
+    assert_parity(got, ref, dtype, f"{N},{d},{V},{K},{dtype},{chunk}")
+
+
+def test_neg_inf_logprob_contributes_nothing(kd):
+    H, W, idx, logp = _case(96, 64, 700, 6, "f32", seed=5)
+    logp = logp.clone()
+    logp[::3, -1] = float("-inf")
+    logp[1, :] = float("-inf")  # a row with no teacher mass at all
+    got = run_hip(kd, H, W, idx, logp, 32)
+    ref = oracle.fused_kl_reference(H, W, idx, logp)
+    assert_parity(got, ref, "f32", "-inf")
+
+
+def test_teacher_equal_to_student_gives_zero_loss(kd):
+    H, W, _, _ = _case(64, 32, 500, 8, "f32", seed=6)
+    logq = torch.log_softmax(H.double() @ W.double().T, dim=1)
+    vals, idx = torch.topk(logq, 8, dim=1)
+    got = run_hip(kd, H, W, idx.to(torch.int32), vals.float(), 16)
+    assert np.abs(got["loss_tok"]).max() < 1e-5
+
+
+def test_dw_accumulate_and_skip_outputs(kd):
+    H, W, idx, logp = _case(100, 64, 333, 4, "f32", seed=7)
+    Hd, Wd, id_, lp = _to_dev(H, W, idx, logp)
+    _, _, lse = kd.kl_forward(Hd, Wd, id_, lp, 32)
+    g = torch.ones(1, device=Hd.device)
+    _, dW1 = kd.kl_backward(Hd, Wd, id_, lp, lse, g, 32, need_dH=False)
+    acc = dW1.clone()
+    kd.kl_backward(Hd, Wd, id_, lp, lse, g, 32, need_dH=False, dW_out=acc, accumulate=True)
+    dH_only, none = kd.kl_backward(Hd, Wd, id_, lp, lse, g, 32, need_dW=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.allclose(acc, 2 * dW1, rtol=1e-6, atol=1e-7)
+    ref = oracle.fused_kl_reference(H, W, idx, logp)
+    assert max_norm_err(dH_only.double().cpu().numpy(), ref["dH"]) < 1e-4
+
+
+def test_empty_input(kd):
+    dev = torch.device("cuda:0")
+    H = torch.empty(0, 64, device=dev)
+    W = torch.randn(100, 64, device=dev)
+    idx = torch.empty(0, 4, dtype=torch.int32, device=dev)
+    logp = torch.empty(0, 4, device=dev)
+    loss, tok, lse = kd.kl_forward(H, W, idx, logp, 16)
+    dW_out = torch.full((100, 64), 3.0, device=dev)
+    _, dW = kd.kl_backward(H, W, idx, logp, lse, torch.ones(1, device=dev), 16, dW_out=dW_out)
+    torch.cuda.synchronize()
+    assert loss.item() == 0.0 and tok.numel() == 0
+    assert torch.count_nonzero(dW).item() == 0
+
+
+def test_bitwise_deterministic(kd):
+    H, W, idx, logp = _case(300, 160, 2000, 100, "bf16", seed=8)
+    a = run_hip(kd, H, W, idx, logp, 128)
+    b = run_hip(kd, H, W, idx, logp, 128)
+    for k in ("loss_tok", "lse", "dH", "dW"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["loss"] == b["loss"]
+
+
+def test_autograd_function(kd):
+    H, W, idx, logp = _case(128, 64, 900, 8, "bf16", seed=9)
+    Hd, Wd, id_, lp = _to_dev(H, W, idx, logp)
+    Hd.requires_grad_(True)
+    Wd.requires_grad_(True)
+    loss = kd.fused_kl(Hd, Wd, id_, lp, chunk=64)
+    (loss * 0.5).backward()
+    torch.cuda.synchronize()
+    ref = oracle.fused_kl_reference(H, W, idx, logp, grad=0.5)
+    assert rel_err(loss.item(), ref["loss"]) < 2e-3
+    assert Hd.grad.dtype == torch.bfloat16 and Wd.grad.dtype == torch.bfloat16
+    assert max_norm_err(Hd.grad.double().cpu().numpy(), ref["dH"]) < 2e-2
+    assert max_norm_err(Wd.grad.double().cpu().numpy(), ref["dW"]) < 2e-2
