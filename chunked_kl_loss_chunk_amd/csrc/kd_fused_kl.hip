@@ -30,6 +30,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <vector>
 
 #include "kd_fused_kl.h"
@@ -197,80 +198,103 @@ __global__ __launch_bounds__(256) void k_prep_scatter(const int* __restrict__ id
 // --------------------------------------------------------------------------
 // forward: fused logit tile with online-logsumexp partials and top-K gather
 // --------------------------------------------------------------------------
+// The tile is zᵀ: 256 vocabulary entries (MFMA M, from W) × 256 tokens (MFMA
+// N, from the chunk of H). Each lane holds, for one token column per block,
+// 64 vocabulary values; a token's (max, Σexp) over the tile needs one
+// cross-half shuffle and one exchange between the two waves sharing it.
 struct FwdArgs {
-  RowOp H;  // chunk rows of H
-  RowOp W;
+  RowOp W;  // [V][d]
+  RowOp H;  // chunk rows of H, [rows][d]
   int kt;   // stages along d
-  int tiles_m, tiles_n;
+  int tiles_t, tiles_v;
   int rows, V, K, nVt;
   const int* offsets;
   const uint2* recs;
   float* zhit;     // [C, K]: z at the cached ids
-  float2* part;    // [C_pad, nVt]: (max, Σexp) of each row over each tile
+  float2* part;    // [C_pad, nVt]: (max, Σexp) of each token over each vocabulary tile
 };
+
+// Reads a packed hit record; the record is wave-uniform.
+__device__ __forceinline__ void read_hit(const uint2* recs, int h, int* tok, int* voc, int* k,
+                                         float* p) {
+  const uint2 r = recs[h];
+  const uint32_t x = __builtin_amdgcn_readfirstlane(r.x);
+  *tok = int(x & 255u);
+  *voc = int((x >> 8) & 1023u);
+  *k = int(x >> 18);
+  *p = __uint_as_float(__builtin_amdgcn_readfirstlane(r.y));
+}
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_fwd_logits(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  const int nblk = a.tiles_m * a.tiles_n;
+  __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
+  lds_t* smem = (lds_t*)(smem_raw);
+  const int nblk = a.tiles_t * a.tiles_v;
   const int logical = xcd_logical(blockIdx.x, nblk);
-  const int tm_t = logical % a.tiles_m, tn_t = logical / a.tiles_m;
-  const int m_base = tm_t * kBM, n_base = tn_t * kBN;
+  const int tt = logical % a.tiles_t, vt = logical / a.tiles_t;
+  const int t_base = tt * kBN, v_base = vt * kBM;
 
   Acc acc;
-  gemm_tile<BF16, RowLoader<kBM>, RowOp, RowLoader<kBN>, RowOp>(acc, a.H, m_base, a.W, n_base, 0,
-                                                                 a.kt, smem);
+  gemm_tile<BF16, RowDirect, RowOp, RowDirect, RowOp>(acc, a.W, v_base, a.H, t_base, 0, a.kt, smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % kWM, wn = wave / kWM;
 
   // z at the cached teacher ids that fall in this tile.
-  const int bkt = tm_t * a.nVt + tn_t;
+  const int bkt = tt * a.nVt + vt;
   const int h0 = a.offsets[bkt], h1 = a.offsets[bkt + 1];
   for (int h = h0; h < h1; ++h) {
-    const uint2 r = a.recs[h];
-    const int rl = r.x & 255, cl = (r.x >> 8) & 1023, k = int(r.x >> 18);
-    const int wr = rl - wm * kWTM, wc = cl - wn * kWTN;
+    int tok, voc, k;
+    float p;
+    read_hit(a.recs, h, &tok, &voc, &k, &p);
+    const int wr = voc - wm * kWTM, wc = tok - wn * kWTN;
     if (unsigned(wr) >= unsigned(kWTM) || unsigned(wc) >= unsigned(kWTN)) continue;
-    int owner, sel;
-    acc_owner(wr, wc, &owner, &sel);
-    const float z = acc_get(acc, sel);
-    if (lane == owner) a.zhit[int64_t(m_base + rl) * a.K + k] = z;
+    const Owner o = acc_owner(wr, wc);
+    float z = 0.f;
+    acc_visit(acc, o.blk, [&](f32x16_t& blk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) z = (i == o.reg) ? blk[i] : z;
+    });
+    if (lane == o.lane) a.zhit[int64_t(t_base + tok) * a.K + k] = z;
   }
 
-  // Row max and Σexp over this tile's valid columns; lanes of one half share rows.
-  float2* red = reinterpret_cast<float2*>(smem);  // [kWN][kBM]
-  bool colok[kTN];
+  // Per token: max and Σexp over this tile's valid vocabulary rows.
+  const int vlim = a.V - (v_base + wm * kWTM);  // rows of this wave below vlim are valid
+  float2* red = reinterpret_cast<float2*>(smem_raw);  // [kWM][kBN]
 #pragma unroll
-  for (int b = 0; b < kTN; ++b) colok[b] = n_base + acc_col(wn, b, lane) < a.V;
+  for (int b = 0; b < kTN; ++b) {
+    float m = kNegInf;
 #pragma unroll
-  for (int tm = 0; tm < kTM; ++tm) {
+    for (int t = 0; t < kTM; ++t)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float m = kNegInf;
+      for (int i = 0; i < 16; ++i) {
+        const int r = t * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        m = r < vlim ? fmaxf(m, acc[t][b][i]) : m;
+      }
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const float ms = m == kNegInf ? 0.f : m;
+    float s = 0.f;
 #pragma unroll
-      for (int b = 0; b < kTN; ++b) m = colok[b] ? fmaxf(m, acc[tm][b][i]) : m;
+    for (int t = 0; t < kTM; ++t)
 #pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      const float ms = m == kNegInf ? 0.f : m;
-      float s = 0.f;
-#pragma unroll
-      for (int b = 0; b < kTN; ++b) s += colok[b] ? __expf(acc[tm][b][i] - ms) : 0.f;
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-      if ((lane & 31) == 0) red[wn * kBM + acc_row(wm, tm, i, lane)] = make_float2(m, s);
-    }
+      for (int i = 0; i < 16; ++i) {
+        const int r = t * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        s += r < vlim ? __expf(acc[t][b][i] - ms) : 0.f;
+      }
+    s += __shfl_xor(s, 32);
+    if (lane < 32) red[wm * kBN + acc_col(wn, b, lane)] = make_float2(m, s);
   }
   __syncthreads();
-  if (tid < kBM && m_base + tid < a.rows) {
+  if (t_base + tid < a.rows) {
     float m = red[tid].x, s = red[tid].y;
 #pragma unroll
-    for (int w = 1; w < kWN; ++w) lse_merge(m, s, red[w * kBM + tid].x, red[w * kBM + tid].y);
-    a.part[int64_t(m_base + tid) * a.nVt + tn_t] = make_float2(m, s);
+    for (int w = 1; w < kWM; ++w) lse_merge(m, s, red[w * kBN + tid].x, red[w * kBN + tid].y);
+    a.part[int64_t(t_base + tid) * a.nVt + vt] = make_float2(m, s);
   }
 }
 
-// One wave per row: lse_r from the tile partials (fixed order), then
+// One wave per token: lse_r from the tile partials (fixed order), then
 // L_r = Σ_k p_k logp_k − Σ_k p_k z_k + S_r lse_r.
 __global__ __launch_bounds__(256) void k_fwd_combine(const float2* __restrict__ part, int nVt,
                                                      const float* __restrict__ zhit,
@@ -320,180 +344,229 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const float2* __restrict__ 
 // backward: recompute the logit tile and turn it into dlogits in registers
 // --------------------------------------------------------------------------
 struct DlArgs {
-  RowOp H;
   RowOp W;
+  RowOp H;
   int kt;
-  int tiles_m, tiles_n;
+  int tiles_t, tiles_v;
   int rows, V, nVt;
   const int* offsets;
   const uint2* recs;
   const float* lse;   // chunk's lse (forward output)
   const float* rowS;  // chunk's S_r
   const float* grad;  // device scalar g
-  void* dl;           // [C_pad, V_pad] of the compute dtype
+  void* dl;           // [C_pad, V_pad] of the compute dtype, token-major
   int64_t ld_dl;      // elements
 };
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs a) {
   typedef typename Elt<BF16>::T T;
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  const int nblk = a.tiles_m * a.tiles_n;
+  __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
+  lds_t* smem = (lds_t*)(smem_raw);
+  const int nblk = a.tiles_t * a.tiles_v;
   const int logical = xcd_logical(blockIdx.x, nblk);
-  const int tm_t = logical % a.tiles_m, tn_t = logical / a.tiles_m;
-  const int m_base = tm_t * kBM, n_base = tn_t * kBN;
+  const int tt = logical % a.tiles_t, vt = logical / a.tiles_t;
+  const int t_base = tt * kBN, v_base = vt * kBM;
 
   Acc acc;
-  gemm_tile<BF16, RowLoader<kBM>, RowOp, RowLoader<kBN>, RowOp>(acc, a.H, m_base, a.W, n_base, 0,
-                                                                 a.kt, smem);
+  gemm_tile<BF16, RowDirect, RowOp, RowDirect, RowOp>(acc, a.W, v_base, a.H, t_base, 0, a.kt, smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % kWM, wn = wave / kWM;
   const float g = *a.grad;
+  const int vlim = a.V - (v_base + wm * kWTM);
 
-  bool colok[kTN];
 #pragma unroll
-  for (int b = 0; b < kTN; ++b) colok[b] = n_base + acc_col(wn, b, lane) < a.V;
+  for (int b = 0; b < kTN; ++b) {
+    const int tok = t_base + acc_col(wn, b, lane);
+    const bool tok_ok = tok < a.rows;
+    const float l = tok_ok ? a.lse[tok] : 0.f;
+    const float gs = tok_ok ? g * a.rowS[tok] : 0.f;
 #pragma unroll
-  for (int tm = 0; tm < kTM; ++tm) {
+    for (int t = 0; t < kTM; ++t)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = m_base + acc_row(wm, tm, i, lane);
-      const bool rok = row < a.rows;
-      const float l = rok ? a.lse[row] : 0.f;
-      const float gs = rok ? g * a.rowS[row] : 0.f;
-#pragma unroll
-      for (int b = 0; b < kTN; ++b)
-        acc[tm][b][i] = (rok && colok[b]) ? gs * __expf(acc[tm][b][i] - l) : 0.f;
-    }
+      for (int i = 0; i < 16; ++i) {
+        const int r = t * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        acc[t][b][i] = (tok_ok && r < vlim) ? gs * __expf(acc[t][b][i] - l) : 0.f;
+      }
   }
 
   // Subtract g·p at the cached ids of this tile.
-  const int bkt = tm_t * a.nVt + tn_t;
+  const int bkt = tt * a.nVt + vt;
   const int h0 = a.offsets[bkt], h1 = a.offsets[bkt + 1];
   for (int h = h0; h < h1; ++h) {
-    const uint2 r = a.recs[h];
-    const int rl = r.x & 255, cl = (r.x >> 8) & 1023;
-    const int wr = rl - wm * kWTM, wc = cl - wn * kWTN;
+    int tok, voc, k;
+    float p;
+    read_hit(a.recs, h, &tok, &voc, &k, &p);
+    const int wr = voc - wm * kWTM, wc = tok - wn * kWTN;
     if (unsigned(wr) >= unsigned(kWTM) || unsigned(wc) >= unsigned(kWTN)) continue;
-    int owner, sel;
-    acc_owner(wr, wc, &owner, &sel);
-    acc_sub(acc, sel, lane == owner ? g * __uint_as_float(r.y) : 0.f);
+    const Owner o = acc_owner(wr, wc);
+    const float x = lane == o.lane ? g * p : 0.f;
+    acc_visit(acc, o.blk, [&](f32x16_t& blk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) blk[i] = (i == o.reg) ? blk[i] - x : blk[i];
+    });
   }
 
+  // Store: four consecutive vocabulary entries of one token per lane.
   T* dl = reinterpret_cast<T*>(a.dl);
 #pragma unroll
-  for (int tm = 0; tm < kTM; ++tm)
+  for (int b = 0; b < kTN; ++b) {
+    const int64_t tok = t_base + acc_col(wn, b, lane);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t row = m_base + acc_row(wm, tm, i, lane);
+    for (int t = 0; t < kTM; ++t)
 #pragma unroll
-      for (int b = 0; b < kTN; ++b) dl[row * a.ld_dl + n_base + acc_col(wn, b, lane)] = T(acc[tm][b][i]);
-    }
+      for (int q = 0; q < 4; ++q) {
+        T* dst = dl + tok * a.ld_dl + v_base + acc_row(wm, t, 4 * q, lane);
+        if constexpr (BF16) {
+          const uint32_t lo = uint32_t(__builtin_bit_cast(uint16_t, __bf16(acc[t][b][4 * q + 0]))) |
+                              (uint32_t(__builtin_bit_cast(uint16_t, __bf16(acc[t][b][4 * q + 1]))) << 16);
+          const uint32_t hi = uint32_t(__builtin_bit_cast(uint16_t, __bf16(acc[t][b][4 * q + 2]))) |
+                              (uint32_t(__builtin_bit_cast(uint16_t, __bf16(acc[t][b][4 * q + 3]))) << 16);
+          *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<float4*>(dst) = make_float4(acc[t][b][4 * q], acc[t][b][4 * q + 1],
+                                                        acc[t][b][4 * q + 2], acc[t][b][4 * q + 3]);
+        }
+      }
+  }
 }
 
 // --------------------------------------------------------------------------
-// dH = dl · W   (A = dl [C_pad, V_pad] rows; B = W [V, d] as [K][cols])
+// dHᵀ = Wᵀ · dlᵀ   (A = W as [K=V][cols=d]; B = dl as [tokens][K=V_pad])
 // --------------------------------------------------------------------------
 struct DhArgs {
-  RowOp dl;
   ColOp W;
-  int tiles_m, tiles_n, splits, kt_total;
+  RowOp dl;
+  int tiles_t, tiles_d, splits, kt_total;
   int rows, d;
   void* dH;          // chunk rows of dH, used when splits == 1
   float* part;       // [splits, C_pad, d] fp32 partials, used when splits > 1
   int64_t part_stride;
 };
 
-template <bool BF16>
+template <bool BF16, class LA>
 __global__ __launch_bounds__(kThreads) void k_bwd_dh(DhArgs a) {
   typedef typename Elt<BF16>::T T;
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  const int nblk = a.tiles_m * a.tiles_n * a.splits;
+  __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
+  lds_t* smem = (lds_t*)(smem_raw);
+  const int nblk = a.tiles_t * a.tiles_d * a.splits;
   const int logical = xcd_logical(blockIdx.x, nblk);
-  const int tm_t = logical % a.tiles_m;
-  const int rest = logical / a.tiles_m;
-  const int tn_t = rest % a.tiles_n, split = rest / a.tiles_n;
+  const int tt = logical % a.tiles_t;
+  const int rest = logical / a.tiles_t;
+  const int dt = rest % a.tiles_d, split = rest / a.tiles_d;
   const int kt0 = int(int64_t(split) * a.kt_total / a.splits);
   const int kt1 = int(int64_t(split + 1) * a.kt_total / a.splits);
-  const int m_base = tm_t * kBM, n_base = tn_t * kBN;
+  const int d_base = dt * kBM, t_base = tt * kBN;
 
   Acc acc;
-  gemm_tile<BF16, RowLoader<kBM>, RowOp, ColLoader<BF16, kBN>, ColOp>(acc, a.dl, m_base, a.W, n_base,
-                                                                      kt0, kt1, smem);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  gemm_tile<BF16, LA, ColOp, RowDirect, RowOp>(acc, a.W, d_base, a.dl, t_base, kt0, kt1, smem);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % kWM, wn = wave / kWM;
 #pragma unroll
-  for (int tm = 0; tm < kTM; ++tm)
+  for (int b = 0; b < kTN; ++b) {
+    const int tok = t_base + acc_col(wn, b, lane);
+    if (tok >= a.rows) continue;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = m_base + acc_row(wm, tm, i, lane);
-      if (row >= a.rows) continue;
+    for (int t = 0; t < kTM; ++t)
 #pragma unroll
-      for (int b = 0; b < kTN; ++b) {
-        const int col = n_base + acc_col(wn, b, lane);
-        if (col >= a.d) continue;
-        const int64_t o = int64_t(row) * a.d + col;
-        if (a.splits == 1)
-          reinterpret_cast<T*>(a.dH)[o] = T(acc[tm][b][i]);
-        else
-          a.part[split * a.part_stride + o] = acc[tm][b][i];
+      for (int q = 0; q < 4; ++q) {
+        const int dd = d_base + acc_row(wm, t, 4 * q, lane);
+        if (dd >= a.d) continue;
+        const int64_t o = int64_t(tok) * a.d + dd;
+        const float4 v = make_float4(acc[t][b][4 * q], acc[t][b][4 * q + 1], acc[t][b][4 * q + 2],
+                                     acc[t][b][4 * q + 3]);
+        if (a.splits > 1) {
+          *reinterpret_cast<float4*>(a.part + split * a.part_stride + o) = v;
+        } else if constexpr (BF16) {
+          const uint32_t lo = uint32_t(__builtin_bit_cast(uint16_t, __bf16(v.x))) |
+                              (uint32_t(__builtin_bit_cast(uint16_t, __bf16(v.y))) << 16);
+          const uint32_t hi = uint32_t(__builtin_bit_cast(uint16_t, __bf16(v.z))) |
+                              (uint32_t(__builtin_bit_cast(uint16_t, __bf16(v.w))) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<T*>(a.dH) + o) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<float4*>(reinterpret_cast<T*>(a.dH) + o) = v;
+        }
       }
-    }
+  }
 }
 
-// Sum the dH split partials in split order and write dH.
+// Sum the dH split partials in split order and write dH (4 elements per thread).
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_bwd_dh_reduce(const float* __restrict__ part, int splits,
-                                                       int64_t stride, int64_t n, void* dH) {
+                                                       int64_t stride, int64_t n4, void* dH) {
   typedef typename Elt<BF16>::T T;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n4;
        i += int64_t(gridDim.x) * blockDim.x) {
-    float s = 0.f;
-    for (int sp = 0; sp < splits; ++sp) s += part[sp * stride + i];
-    reinterpret_cast<T*>(dH)[i] = T(s);
+    float4 s = reinterpret_cast<const float4*>(part)[i];
+    for (int sp = 1; sp < splits; ++sp) {
+      const float4 v = reinterpret_cast<const float4*>(part + sp * stride)[i];
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    T* o = reinterpret_cast<T*>(dH) + 4 * i;
+    o[0] = T(s.x);
+    o[1] = T(s.y);
+    o[2] = T(s.z);
+    o[3] = T(s.w);
   }
 }
 
 // --------------------------------------------------------------------------
-// dW (+)= dlᵀ · H_c   (A = dl as [K=C][cols=V]; B = H_c as [K=C][cols=d])
+// dWᵀ (+)= H_cᵀ · dl   (A = H_c as [K=tokens][cols=d]; B = dl as [K=tokens][cols=V_pad])
 // --------------------------------------------------------------------------
 struct DwArgs {
-  ColOp dl;
   ColOp H;
-  int tiles_m, tiles_n, kt;
+  ColOp dl;
+  int tiles_d, tiles_v, kt;
   int V, d;
   float* dW;
   int beta;  // 0: overwrite, 1: accumulate
 };
 
-template <bool BF16>
+template <bool BF16, class LC>
 __global__ __launch_bounds__(kThreads) void k_bwd_dw(DwArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  const int nblk = a.tiles_m * a.tiles_n;
+  __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
+  lds_t* smem = (lds_t*)(smem_raw);
+  const int nblk = a.tiles_d * a.tiles_v;
   const int logical = xcd_logical(blockIdx.x, nblk);
-  const int tn_t = logical % a.tiles_n, tm_t = logical / a.tiles_n;
-  const int m_base = tm_t * kBM, n_base = tn_t * kBN;
+  const int dt = logical % a.tiles_d, vt = logical / a.tiles_d;
+  const int d_base = dt * kBM, v_base = vt * kBN;
 
   Acc acc;
-  gemm_tile<BF16, ColLoader<BF16, kBM>, ColOp, ColLoader<BF16, kBN>, ColOp>(acc, a.dl, m_base, a.H,
-                                                                            n_base, 0, a.kt, smem);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  gemm_tile<BF16, LC, ColOp, LC, ColOp>(acc, a.H, d_base, a.dl, v_base, 0, a.kt, smem);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % kWM, wn = wave / kWM;
 #pragma unroll
-  for (int tm = 0; tm < kTM; ++tm)
+  for (int b = 0; b < kTN; ++b) {
+    const int v = v_base + acc_col(wn, b, lane);
+    if (v >= a.V) continue;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = m_base + acc_row(wm, tm, i, lane);
-      if (row >= a.V) continue;
+    for (int t = 0; t < kTM; ++t)
 #pragma unroll
-      for (int b = 0; b < kTN; ++b) {
-        const int col = n_base + acc_col(wn, b, lane);
-        if (col >= a.d) continue;
-        float* p = a.dW + int64_t(row) * a.d + col;
-        *p = a.beta ? *p + acc[tm][b][i] : acc[tm][b][i];
+      for (int q = 0; q < 4; ++q) {
+        const int dd = d_base + acc_row(wm, t, 4 * q, lane);
+        if (dd >= a.d) continue;
+        float4* p = reinterpret_cast<float4*>(a.dW + int64_t(v) * a.d + dd);
+        float4 x = make_float4(acc[t][b][4 * q], acc[t][b][4 * q + 1], acc[t][b][4 * q + 2],
+                               acc[t][b][4 * q + 3]);
+        if (a.beta) {
+          const float4 y = *p;
+          x.x += y.x;
+          x.y += y.y;
+          x.z += y.z;
+          x.w += y.w;
+        }
+        *p = x;
       }
-    }
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -539,9 +612,9 @@ void timed(int cls, hipStream_t st, F&& launch) {
     return;
   }
   hipEvent_t a = timing_event(), b = timing_event();
-  if (a) hipEventRecord(a, st);
+  if (a) (void)hipEventRecord(a, st);
   launch();
-  if (b) hipEventRecord(b, st);
+  if (b) (void)hipEventRecord(b, st);
   if (a && b) g_timing_recs.push_back(TimingRec{cls, a, b});
 }
 
@@ -567,6 +640,9 @@ void launch_reset(const Plan& p, const Ws& ws, hipStream_t st) {
 }
 
 template <bool BF16>
+using ColLoad = typename std::conditional<BF16, ColDirect, ColReg>::type;
+
+template <bool BF16>
 int run_fwd(const Plan& p, const void* H, const void* W, const int32_t* idx, const float* logp,
             float* loss_tok, float* lse, float* loss_sum, void* workspace, hipStream_t st) {
   Ws ws{static_cast<char*>(workspace), p};
@@ -578,11 +654,11 @@ int run_fwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
       const int rows = int(p.N - r0 < p.C ? p.N - r0 : p.C);
       launch_prep(p, ws, idx, logp, r0, rows, st);
       FwdArgs a;
-      a.H = RowOp{static_cast<const char*>(H) + r0 * row_bytes, row_bytes, rows, int(row_bytes)};
       a.W = RowOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
+      a.H = RowOp{static_cast<const char*>(H) + r0 * row_bytes, row_bytes, rows, int(row_bytes)};
       a.kt = int(p.kt_d);
-      a.tiles_m = int(cdiv(rows, kBM));
-      a.tiles_n = int(p.nVt);
+      a.tiles_t = int(cdiv(rows, kBN));
+      a.tiles_v = int(p.nVt);
       a.rows = rows;
       a.V = int(p.V);
       a.K = int(p.K);
@@ -592,7 +668,7 @@ int run_fwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
       a.zhit = ws.at<float>(p.off_zhit);
       a.part = ws.at<float2>(p.off_part);
       timed(KD_KERNEL_FWD_LOGITS, st, [&] {
-        hipLaunchKernelGGL(k_fwd_logits<BF16>, dim3(a.tiles_m * a.tiles_n), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL(k_fwd_logits<BF16>, dim3(a.tiles_t * a.tiles_v), dim3(kThreads), 0, st,
                            a);
       });
       timed(KD_KERNEL_OTHER, st, [&] {
@@ -617,19 +693,21 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
   }
   launch_reset(p, ws, st);
   const int64_t row_bytes = p.d * p.es;
-  const int kBKe = kLdsRow / p.es;
+  const int k_per_stage = kLdsRow / p.es;
+  auto dh_kernel = k_bwd_dh<BF16, ColLoad<BF16>>;
+  auto dw_kernel = k_bwd_dw<BF16, ColLoad<BF16>>;
   for (int64_t r0 = 0; r0 < p.N; r0 += p.C) {
     const int rows = int(p.N - r0 < p.C ? p.N - r0 : p.C);
     launch_prep(p, ws, idx, logp, r0, rows, st);
     const char* Hc = static_cast<const char*>(H) + r0 * row_bytes;
-    const int tiles_m = int(cdiv(rows, kBM));
+    const int tiles_t = int(cdiv(rows, kBN));
 
     DlArgs a;
-    a.H = RowOp{Hc, row_bytes, rows, int(row_bytes)};
     a.W = RowOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
+    a.H = RowOp{Hc, row_bytes, rows, int(row_bytes)};
     a.kt = int(p.kt_d);
-    a.tiles_m = tiles_m;
-    a.tiles_n = int(p.nVt);
+    a.tiles_t = tiles_t;
+    a.tiles_v = int(p.nVt);
     a.rows = rows;
     a.V = int(p.V);
     a.nVt = int(p.nVt);
@@ -641,17 +719,17 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
     a.dl = ws.at<char>(p.off_dl);
     a.ld_dl = p.V_pad;
     timed(KD_KERNEL_BWD_DLOGITS, st, [&] {
-      hipLaunchKernelGGL(k_bwd_dlogits<BF16>, dim3(a.tiles_m * a.tiles_n), dim3(kThreads), 0, st,
+      hipLaunchKernelGGL(k_bwd_dlogits<BF16>, dim3(a.tiles_t * a.tiles_v), dim3(kThreads), 0, st,
                          a);
     });
 
     const int64_t dl_ld_bytes = p.V_pad * p.es;
     if (dH) {
       DhArgs h;
-      h.dl = RowOp{ws.at<char>(p.off_dl), dl_ld_bytes, rows, int(dl_ld_bytes)};
       h.W = ColOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
-      h.tiles_m = tiles_m;
-      h.tiles_n = int(cdiv(p.d, kBN));
+      h.dl = RowOp{ws.at<char>(p.off_dl), dl_ld_bytes, rows, int(dl_ld_bytes)};
+      h.tiles_t = tiles_t;
+      h.tiles_d = int(cdiv(p.d, kBM));
       h.splits = p.dh_splits;
       h.kt_total = int(p.kt_v);
       h.rows = rows;
@@ -660,31 +738,31 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
       h.part = p.dh_splits > 1 ? ws.at<float>(p.off_dhpart) : nullptr;
       h.part_stride = p.C_pad * p.d;
       timed(KD_KERNEL_BWD_DH, st, [&] {
-        hipLaunchKernelGGL(k_bwd_dh<BF16>, dim3(h.tiles_m * h.tiles_n * h.splits), dim3(kThreads),
-                           0, st, h);
+        hipLaunchKernelGGL(dh_kernel, dim3(h.tiles_t * h.tiles_d * h.splits), dim3(kThreads), 0, st,
+                           h);
       });
       if (p.dh_splits > 1) {
-        const int64_t n = int64_t(rows) * p.d;
-        const int nb = int(cdiv(n, 256) < 4096 ? cdiv(n, 256) : 4096);
+        const int64_t n4 = int64_t(rows) * p.d / 4;
+        const int nb = int(cdiv(n4, 256) < 4096 ? cdiv(n4, 256) : 4096);
         timed(KD_KERNEL_OTHER, st, [&] {
           hipLaunchKernelGGL(k_bwd_dh_reduce<BF16>, dim3(nb), dim3(256), 0, st, h.part, h.splits,
-                             h.part_stride, n, h.dH);
+                             h.part_stride, n4, h.dH);
         });
       }
     }
     if (dW) {
       DwArgs w;
-      w.dl = ColOp{ws.at<char>(p.off_dl), dl_ld_bytes, rows, int(dl_ld_bytes)};
       w.H = ColOp{Hc, row_bytes, rows, int(row_bytes)};
-      w.tiles_m = int(cdiv(p.V, kBM));
-      w.tiles_n = int(cdiv(p.d, kBN));
-      w.kt = int(cdiv(rows, kBKe));
+      w.dl = ColOp{ws.at<char>(p.off_dl), dl_ld_bytes, rows, int(dl_ld_bytes)};
+      w.tiles_d = int(cdiv(p.d, kBM));
+      w.tiles_v = int(cdiv(p.V, kBN));
+      w.kt = int(cdiv(rows, k_per_stage));
       w.V = int(p.V);
       w.d = int(p.d);
       w.dW = dW;
       w.beta = (accumulate || r0 > 0) ? 1 : 0;
       timed(KD_KERNEL_BWD_DW, st, [&] {
-        hipLaunchKernelGGL(k_bwd_dw<BF16>, dim3(w.tiles_m * w.tiles_n), dim3(kThreads), 0, st, w);
+        hipLaunchKernelGGL(dw_kernel, dim3(w.tiles_d * w.tiles_v), dim3(kThreads), 0, st, w);
       });
     }
   }

@@ -47,7 +47,7 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
 
   // dH = dlogits · W has a short output (C × d) and a long contraction (V):
   // split the contraction so that enough workgroups exist to fill the chip.
-  const int64_t tiles_mn = q.nMt * cdiv(d, kTileN);
+  const int64_t tiles_mn = q.nMt * cdiv(d, 256);
   int64_t splits = cdiv(kDhTargetTiles, tiles_mn);
   if (splits > kMaxDhSplits) splits = kMaxDhSplits;
   if (splits > q.kt_v) splits = q.kt_v;

@@ -8,18 +8,18 @@
 
 namespace kd {
 
-// Tile of the logit GEMM (rows of a chunk × vocabulary columns). The top-K
+// Tile of the logit GEMM (tokens of a chunk × vocabulary entries). The top-K
 // hit lists are bucketed by this tile, so the plan fixes it.
-constexpr int kTileM = 128;
-constexpr int kTileN = 128;
+constexpr int kTileM = 256;  // tokens
+constexpr int kTileN = 256;  // vocabulary
 // Bytes of the contraction dimension staged per LDS row and pipeline stage.
 constexpr int kStageBytes = 128;
-// Packed hit record: row-in-tile (8 bits), column-in-tile (10 bits), k (14 bits).
+// Packed hit record: token-in-tile (8 bits), vocab-in-tile (10 bits), k (14 bits).
 constexpr int64_t kMaxK = (1 << 14) - 1;
 // Upper bound on the dH split-K factor.
 constexpr int kMaxDhSplits = 32;
-// Target number of dH workgroups per chunk (a few waves of the 256 CUs).
-constexpr int kDhTargetTiles = 1024;
+// Target number of dH workgroups per chunk (three waves of the 256 CUs).
+constexpr int kDhTargetTiles = 768;
 
 struct Plan {
   int64_t N, d, V, K, chunk;
