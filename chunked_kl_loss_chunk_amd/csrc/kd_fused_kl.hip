@@ -214,15 +214,62 @@ struct FwdArgs {
   float2* part;    // [C_pad, nVt]: (max, Σexp) of each token over each vocabulary tile
 };
 
-// Reads a packed hit record; the record is wave-uniform.
-__device__ __forceinline__ void read_hit(const uint2* recs, int h, int* tok, int* voc, int* k,
-                                         float* p) {
-  const uint2 r = recs[h];
-  const uint32_t x = __builtin_amdgcn_readfirstlane(r.x);
-  *tok = int(x & 255u);
-  *voc = int((x >> 8) & 1023u);
-  *k = int(x >> 18);
-  *p = __uint_as_float(__builtin_amdgcn_readfirstlane(r.y));
+// Hit records of one tile. The epilogue starts by loading the first 64
+// records (one coalesced 8-byte load per lane) so their latency overlaps the
+// epilogue's other work; each wave then keeps the records that fall in its
+// 128×128 quadrant (a ballot) and visits them one by one with uniform
+// readlanes, so no record costs a dependent memory access.
+struct TileHits {
+  const uint2* recs;
+  int h0, n;
+  uint2 first;  // record h0 + lane, if lane < n
+};
+
+__device__ __forceinline__ TileHits hits_begin(const int* offsets, const uint2* recs, int bkt,
+                                               int lane) {
+  TileHits t;
+  t.recs = recs;
+  t.h0 = offsets[bkt];
+  t.n = offsets[bkt + 1] - t.h0;
+  t.first = lane < t.n ? recs[t.h0 + lane] : make_uint2(0xffffffffu, 0u);
+  return t;
+}
+
+// Records base..base+63 (one per lane) and the ballot of those in this
+// wave's quadrant.
+__device__ __forceinline__ uint2 hits_load(const TileHits& t, int base, int lane) {
+  const int i = base + lane;
+  return base == 0 ? t.first : (i < t.n ? t.recs[t.h0 + i] : make_uint2(0xffffffffu, 0u));
+}
+__device__ __forceinline__ uint64_t hits_mine(const TileHits& t, const uint2& r, int base, int wm,
+                                              int wn, int lane) {
+  const int wr = int((r.x >> 8) & 1023u) - wm * kWTM;  // vocabulary row in the wave's quadrant
+  const int wc = int(r.x & 255u) - wn * kWTN;          // token column in the wave's quadrant
+  return __ballot(base + lane < t.n && unsigned(wr) < unsigned(kWTM) && unsigned(wc) < unsigned(kWTN));
+}
+
+// Accumulator element `reg` of block `blk` (both wave-uniform).
+__device__ __forceinline__ float acc_pick(const Acc& acc, int blk, int reg) {
+  float v = 0.f;
+#pragma unroll
+  for (int a = 0; a < kTM; ++a)
+#pragma unroll
+    for (int b = 0; b < kTN; ++b)
+      if (blk == a * kTN + b) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v = (i == reg) ? acc[a][b][i] : v;
+      }
+  return v;
+}
+__device__ __forceinline__ void acc_sub_at(Acc& acc, int blk, int reg, float x) {
+#pragma unroll
+  for (int a = 0; a < kTM; ++a)
+#pragma unroll
+    for (int b = 0; b < kTN; ++b)
+      if (blk == a * kTN + b) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][b][i] = (i == reg) ? acc[a][b][i] - x : acc[a][b][i];
+      }
 }
 
 template <bool BF16>
@@ -242,21 +289,19 @@ __global__ __launch_bounds__(kThreads) void k_fwd_logits(FwdArgs a) {
   const int wm = wave % kWM, wn = wave / kWM;
 
   // z at the cached teacher ids that fall in this tile.
-  const int bkt = tt * a.nVt + vt;
-  const int h0 = a.offsets[bkt], h1 = a.offsets[bkt + 1];
-  for (int h = h0; h < h1; ++h) {
-    int tok, voc, k;
-    float p;
-    read_hit(a.recs, h, &tok, &voc, &k, &p);
-    const int wr = voc - wm * kWTM, wc = tok - wn * kWTN;
-    if (unsigned(wr) >= unsigned(kWTM) || unsigned(wc) >= unsigned(kWTN)) continue;
-    const Owner o = acc_owner(wr, wc);
-    float z = 0.f;
-    acc_visit(acc, o.blk, [&](f32x16_t& blk) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) z = (i == o.reg) ? blk[i] : z;
-    });
-    if (lane == o.lane) a.zhit[int64_t(t_base + tok) * a.K + k] = z;
+  const TileHits hits = hits_begin(a.offsets, a.recs, tt * a.nVt + vt, lane);
+  for (int base = 0; base < hits.n; base += 64) {
+    const uint2 r = hits_load(hits, base, lane);
+    uint64_t mask = hits_mine(hits, r, base, wm, wn, lane);
+    while (mask) {
+      const int j = __builtin_ctzll(mask);
+      mask &= mask - 1;
+      const uint32_t x = __builtin_amdgcn_readlane(r.x, j);
+      const int tok = int(x & 255u), voc = int((x >> 8) & 1023u), k = int(x >> 18);
+      const Owner o = acc_owner(voc - wm * kWTM, tok - wn * kWTN);
+      const float z = acc_pick(acc, o.blk, o.reg);
+      if (lane == o.lane) a.zhit[int64_t(t_base + tok) * a.K + k] = z;
+    }
   }
 
   // Per token: max and Σexp over this tile's valid vocabulary rows.
@@ -376,6 +421,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs a) {
   const int wm = wave % kWM, wn = wave / kWM;
   const float g = *a.grad;
   const int vlim = a.V - (v_base + wm * kWTM);
+  const TileHits hits = hits_begin(a.offsets, a.recs, tt * a.nVt + vt, lane);
 
 #pragma unroll
   for (int b = 0; b < kTN; ++b) {
@@ -390,23 +436,6 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs a) {
         const int r = t * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
         acc[t][b][i] = (tok_ok && r < vlim) ? gs * __expf(acc[t][b][i] - l) : 0.f;
       }
-  }
-
-  // Subtract g·p at the cached ids of this tile.
-  const int bkt = tt * a.nVt + vt;
-  const int h0 = a.offsets[bkt], h1 = a.offsets[bkt + 1];
-  for (int h = h0; h < h1; ++h) {
-    int tok, voc, k;
-    float p;
-    read_hit(a.recs, h, &tok, &voc, &k, &p);
-    const int wr = voc - wm * kWTM, wc = tok - wn * kWTN;
-    if (unsigned(wr) >= unsigned(kWTM) || unsigned(wc) >= unsigned(kWTN)) continue;
-    const Owner o = acc_owner(wr, wc);
-    const float x = lane == o.lane ? g * p : 0.f;
-    acc_visit(acc, o.blk, [&](f32x16_t& blk) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) blk[i] = (i == o.reg) ? blk[i] - x : blk[i];
-    });
   }
 
   // Store: four consecutive vocabulary entries of one token per lane.
@@ -430,6 +459,23 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs a) {
                                                         acc[t][b][4 * q + 2], acc[t][b][4 * q + 3]);
         }
       }
+  }
+  // At the cached ids of this tile the value is S_r q − p, not S_r q: the
+  // lane that owns the element stores the corrected value over the one it
+  // just wrote (same thread, same address: the later store wins).
+  for (int base = 0; base < hits.n; base += 64) {
+    const uint2 r = hits_load(hits, base, lane);
+    uint64_t mask = hits_mine(hits, r, base, wm, wn, lane);
+    while (mask) {
+      const int j = __builtin_ctzll(mask);
+      mask &= mask - 1;
+      const uint32_t x = __builtin_amdgcn_readlane(r.x, j);
+      const float p = __uint_as_float(__builtin_amdgcn_readlane(r.y, j));
+      const int tok = int(x & 255u), voc = int((x >> 8) & 1023u);
+      const Owner o = acc_owner(voc - wm * kWTM, tok - wn * kWTN);
+      const float v = acc_pick(acc, o.blk, o.reg) - g * p;
+      if (lane == o.lane) dl[int64_t(t_base + tok) * a.ld_dl + v_base + voc] = T(v);
+    }
   }
 }
 

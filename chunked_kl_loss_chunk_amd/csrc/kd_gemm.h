@@ -13,15 +13,16 @@
 //
 // A workgroup of 256 threads (4 wave64s, 2×2) owns a 256×256 output tile;
 // each wave owns 128×128 as 4×4 blocks of the 32×32 MFMA (256 fp32
-// accumulators per lane). The contraction is staged through LDS 128 bytes per
-// row at a time (64 bf16 or 32 fp32), two stages in flight (128 KiB of LDS).
-// Operands are copied global→LDS by the LDS-DMA path (global_load_lds, 16
-// bytes per lane, no VGPRs), in one of two layouts:
+// accumulators per lane). The contraction is staged through LDS 64 bytes per
+// row at a time (32 bf16 or 16 fp32) in a ring of four stages (128 KiB of
+// LDS), three of them in flight while the fourth is consumed. Operands are
+// copied global→LDS by the LDS-DMA path (global_load_lds, 16 bytes per lane,
+// no VGPRs), in one of two layouts:
 //
-//   RowDirect  operand stored [rows][K] (K contiguous). LDS [256 rows][128 B],
+//   RowDirect  operand stored [rows][K] (K contiguous). LDS [256 rows][64 B],
 //              16-byte chunks XOR-swizzled by the row; fragments are
 //              ds_read_b128.
-//   ColDirect  operand stored [K][cols] (cols contiguous), bf16. LDS [64 K][512 B]
+//   ColDirect  operand stored [K][cols] (cols contiguous), bf16. LDS [32 K][512 B]
 //              as in HBM, 32-byte segments XOR-swizzled by K; fragments are
 //              read transposed with ds_read_b64_tr_b16, so the transposed
 //              operands of dH and dW need no copy in HBM and no VALU work.
@@ -49,9 +50,18 @@ constexpr int kBM = 256, kBN = 256;                 // workgroup tile
 constexpr int kWM = 2, kWN = 2;                     // waves along M and N
 constexpr int kWTM = kBM / kWM, kWTN = kBN / kWN;   // 128×128 per wave
 constexpr int kTM = kWTM / 32, kTN = kWTN / 32;     // 4×4 MFMA blocks per wave
-constexpr int kLdsRow = 128;                    // contraction bytes per row and stage
-constexpr int kOpBytes = kBM * kLdsRow;         // one operand tile per stage: 32 KiB
-constexpr int kSmemBytes = 4 * kOpBytes;            // A and B, two stages: 128 KiB
+#ifndef KD_GEMM_ROW
+#define KD_GEMM_ROW 64
+#endif
+constexpr int kLdsRow = KD_GEMM_ROW;                // contraction bytes per row and stage (64 or 128)
+constexpr int kSteps = kLdsRow / 32;                // MFMA steps (16 bytes per lane-half) per stage
+#ifndef KD_GEMM_STAGES
+#define KD_GEMM_STAGES 4
+#endif
+constexpr int kStages = KD_GEMM_STAGES;             // ring of stages in LDS
+constexpr int kOpBytes = kBM * kLdsRow;             // one operand tile per stage: 16 KiB
+constexpr int kStageBytes = 2 * kOpBytes;           // A and B of one stage
+constexpr int kSmemBytes = kStages * kStageBytes;   // 128 KiB with four stages
 
 // Source of out-of-range fetches.
 __device__ __attribute__((aligned(64))) uint4 g_zero16[4];
@@ -75,9 +85,14 @@ struct ColOp {
 };
 
 // Row layout: physical 16-byte chunk of logical chunk c in row `row` is
-// c ^ rswz(row). Eight consecutive rows (one fragment read) hit eight
-// different chunks; so do rows eight apart (the fp32 transposing writes).
-__device__ __forceinline__ int rswz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
+// c ^ rswz(row). A fragment read puts 8 (or 16) consecutive rows on the same
+// logical chunk; rswz gives rows that share a 128-byte (256-byte) bank row
+// distinct chunks. 64-byte rows: two (four) rows per bank row. 128-byte rows:
+// one (two) per bank row.
+__device__ __forceinline__ int rswz(int row) {
+  if constexpr (kLdsRow == 64) return ((row >> 1) ^ (row >> 2)) & 3;
+  return (row & 7) ^ ((row >> 3) & 1);
+}
 
 // Column layout: physical 32-byte segment of logical segment s in K-row k is
 // s ^ cswz(k), cswz = {0, 2, 5, 7} over k mod 4. A transpose read touches
@@ -90,34 +105,42 @@ __device__ __forceinline__ void lds_dma16(const void* src, lds_t* dst_wave_base)
   __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(dst_wave_base), 16, 0, 0);
 }
 
-__device__ __forceinline__ uint4 lds_read16(const lds_t* p) {
-  const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(p);
-  return make_uint4(v[0], v[1], v[2], v[3]);
+__device__ __forceinline__ u32x4_t lds_read16(const lds_t* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(p);
 }
 
 __device__ __forceinline__ void lds_write16(lds_t* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(p) = u32x4_t{a, b, c, d};
 }
 
-__device__ __forceinline__ uint2 lds_read_tr8(const lds_t* p) {
-  s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>(const_cast<lds_t*>(p)));
-  return __builtin_bit_cast(uint2, v);
+// Transposed LDS read (ds_read_b64_tr_b16), issued as inline asm. As an
+// intrinsic the compiler makes it wait for every in-flight LDS-DMA
+// (vmcnt(0)), which would drain the stage pipeline; as asm it is ordered only
+// by the pipeline's own explicit waits and barriers. The compiler does not
+// track its completion either: callers wait with lds_wait_frags() before
+// using the result.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2_t lds_read_tr8(const lds_t* p) {
+  u32x2_t v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(p));
+  return v;
 }
 
 // --------------------------------------------------------------------------
 // operand loaders
 // --------------------------------------------------------------------------
 struct RowDirect {
-  // 256 rows × 128 B = 32 blocks of 8 rows (1 KiB); each wave copies 8 blocks.
+  static constexpr int kDma = kOpBytes / 1024 / 4;  // LDS-DMA instructions per wave and stage
+  static constexpr int kChunks = kLdsRow / 16;       // 16-byte chunks per row
+  // 256 rows × kLdsRow = blocks of 1 KiB (1024/kLdsRow rows); each wave copies kDma blocks.
   __device__ __forceinline__ void fetch(const RowOp& op, int r0, int kt, lds_t* tile, int wave,
                                         int lane, int) {
     const char* zero = reinterpret_cast<const char*>(g_zero16);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int blk = wave * 8 + j;
-      const int row = blk * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ rswz(row);  // logical chunk held at physical chunk lane&7
+    for (int j = 0; j < kDma; ++j) {
+      const int blk = wave * kDma + j;
+      const int row = blk * (1024 / kLdsRow) + lane / kChunks;
+      const int c = (lane % kChunks) ^ rswz(row);  // logical chunk held at physical chunk lane%kChunks
       const int gr = r0 + row, kb = kt * kLdsRow + c * 16;
       const char* src = (gr < op.rows && kb < op.kbytes) ? op.base + int64_t(gr) * op.ld + kb : zero;
       lds_dma16(src, tile + blk * 1024);
@@ -125,23 +148,31 @@ struct RowDirect {
   }
   __device__ __forceinline__ void commit(lds_t*, int) {}
   // Fragment of a 32-row block: lane l holds row rb + l%32, chunk 2s + l/32.
-  __device__ static __forceinline__ uint4 frag(const lds_t* tile, int rb, int s, int lane) {
+  __device__ static __forceinline__ u32x4_t frag(const lds_t* tile, int rb, int s, int lane) {
     const int row = rb + (lane & 31), c = 2 * s + (lane >> 5);
     return lds_read16(tile + row * kLdsRow + ((c ^ rswz(row)) << 4));
+  }
+  // Reads are whole fragments.
+  static constexpr int kReads = 1;
+  __device__ static __forceinline__ void frag_part(u32x4_t& f, const lds_t* tile, int rb, int s,
+                                                   int, int lane) {
+    f = frag(tile, rb, s, lane);
   }
 };
 
 struct ColDirect {  // bf16 only
-  // 64 K-rows × 512 B = 32 blocks of 2 K-rows (1 KiB); each wave copies 8 blocks.
+  static constexpr int kK = kLdsRow / 2;            // contraction rows per stage (32 or 64)
+  static constexpr int kDma = kOpBytes / 1024 / 4;  // LDS-DMA instructions per wave and stage
+  // kK K-rows × 512 B = blocks of 2 K-rows (1 KiB); each wave copies kDma blocks.
   __device__ __forceinline__ void fetch(const ColOp& op, int c0, int kt, lds_t* tile, int wave,
                                         int lane, int) {
     const char* zero = reinterpret_cast<const char*>(g_zero16);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int blk = wave * 8 + j;
+    for (int j = 0; j < kDma; ++j) {
+      const int blk = wave * kDma + j;
       const int k = blk * 2 + (lane >> 5);
       const int lbyte = ((lane & 31) << 4) ^ (cswz(k) << 5);  // logical byte at physical (lane&31)*16
-      const int gk = kt * 64 + k, cb = c0 * 2 + lbyte;
+      const int gk = kt * kK + k, cb = c0 * 2 + lbyte;
       const char* src = (gk < op.krows && cb < op.cbytes) ? op.base + int64_t(gk) * op.ld + cb : zero;
       lds_dma16(src, tile + blk * 1024);
     }
@@ -149,18 +180,24 @@ struct ColDirect {  // bf16 only
   __device__ __forceinline__ void commit(lds_t*, int) {}
   // Fragment of a 32-column block cb..cb+31 at contraction step s (16 K):
   // lane l gets column cb + l%32 and K = 16s + 8(l/32) + 0..7, the same
-  // assignment as RowDirect::frag. Each 16-lane group reads a 4×16 block per
-  // ds_read_b64_tr_b16: lane L addresses K-row L/4, columns 4(L%4)..+3, and
-  // receives column L of the four rows.
-  __device__ static __forceinline__ uint4 frag(const lds_t* tile, int cb, int s, int lane) {
+  // assignment as RowDirect::frag, in two halves of four K. Each 16-lane
+  // group reads a 4×16 block per ds_read_b64_tr_b16: lane L addresses K-row
+  // L/4, columns 4(L%4)..+3, and receives column L of the four rows.
+  static constexpr int kReads = 2;
+  __device__ static __forceinline__ void frag_part(u32x4_t& f, const lds_t* tile, int cb, int s,
+                                                   int half, int lane) {
     const int g = lane >> 4, L = lane & 15;
     const int colb = (cb + 16 * (g & 1) + 4 * (L & 3)) * 2;
     const int seg = colb >> 5, within = colb & 31;
-    const int k0 = s * 16 + 8 * (g >> 1) + (L >> 2);
-    const int k1 = k0 + 4;
-    const uint2 lo = lds_read_tr8(tile + k0 * 512 + ((seg ^ cswz(k0)) << 5) + within);
-    const uint2 hi = lds_read_tr8(tile + k1 * 512 + ((seg ^ cswz(k1)) << 5) + within);
-    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    const int k = s * 16 + 8 * (g >> 1) + 4 * half + (L >> 2);
+    const u32x2_t v = lds_read_tr8(tile + k * 512 + ((seg ^ cswz(k)) << 5) + within);
+    if (half == 0) {
+      f[0] = v[0];
+      f[1] = v[1];
+    } else {
+      f[2] = v[0];
+      f[3] = v[1];
+    }
   }
 };
 
@@ -168,40 +205,41 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-struct ColReg {  // fp32 only: 32 K-rows per stage, 256 columns, row layout in LDS
-  static constexpr int kPer = 2;  // (32/4) K-groups × (256/4) chunks / 256 threads
-  uint4 v[kPer][4];
-  __device__ __forceinline__ void fetch(const ColOp& op, int c0, int kt, lds_t*, int, int, int tid) {
+struct ColReg {  // fp32 only: kLdsRow/4 K-rows per stage, 256 columns, row layout in LDS
+  static constexpr int kDma = 0;
+  static constexpr int kK = kLdsRow / 4;  // contraction rows per stage
+  static constexpr int kPer = (kK / 4) * 64 / kThreads;
+  // (kK/4) K-groups × (256/4) column chunks, kPer per thread. The load is
+  // consumed at once (fp32 is the small, exact path, not the fast one).
+  __device__ __forceinline__ void fetch(const ColOp& op, int c0, int kt, lds_t* tile, int, int,
+                                        int tid) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int u = tid + i * kThreads;
       const int kq = u >> 6, nc = u & 63;
       const int cb = (c0 + nc * 4) * 4;
+      uint4 v[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int k = kt * 32 + 4 * kq + j;
+        const int k = kt * kK + 4 * kq + j;
         if (k < op.krows && cb < op.cbytes)
-          v[i][j] = *reinterpret_cast<const uint4*>(op.base + int64_t(k) * op.ld + cb);
+          v[j] = *reinterpret_cast<const uint4*>(op.base + int64_t(k) * op.ld + cb);
         else
-          v[i][j] = make_uint4(0u, 0u, 0u, 0u);
+          v[j] = make_uint4(0u, 0u, 0u, 0u);
       }
-    }
-  }
-  __device__ __forceinline__ void commit(lds_t* tile, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int u = tid + i * kThreads;
-      const int kq = u >> 6, nc = u & 63;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int n = nc * 4 + e;
-        lds_write16(tile + n * kLdsRow + ((kq ^ rswz(n)) << 4), word(v[i][0], e), word(v[i][1], e),
-                    word(v[i][2], e), word(v[i][3], e));
+        lds_write16(tile + n * kLdsRow + ((kq ^ rswz(n)) << 4), word(v[0], e), word(v[1], e),
+                    word(v[2], e), word(v[3], e));
       }
     }
   }
-  __device__ static __forceinline__ uint4 frag(const lds_t* tile, int rb, int s, int lane) {
-    return RowDirect::frag(tile, rb, s, lane);
+  __device__ __forceinline__ void commit(lds_t*, int) {}
+  static constexpr int kReads = 1;
+  __device__ static __forceinline__ void frag_part(u32x4_t& f, const lds_t* tile, int rb, int s,
+                                                   int, int lane) {
+    f = RowDirect::frag(tile, rb, s, lane);
   }
 };
 
@@ -211,15 +249,15 @@ struct ColReg {  // fp32 only: 32 K-rows per stage, 256 columns, row layout in L
 // so lane-half h covers K = 4h + i. A and B use the same assignment, so each
 // of the 8 K-elements of a chunk pair is summed exactly once.
 template <bool BF16>
-__device__ __forceinline__ void mma(f32x16_t& acc, const uint4& a, const uint4& b) {
+__device__ __forceinline__ void mma(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
   if constexpr (BF16) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                   __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
   } else {
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[e]), __uint_as_float(b[e]), acc,
+                                                 0, 0, 0);
   }
 }
 
@@ -228,65 +266,93 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // Wait until every LDS access of this wave has completed.
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }   // lgkmcnt(0)
 
-// LDS reads one fragment of an operand costs: 1 (ds_read_b128) or 2 (transpose reads).
-template <class L>
-struct FragReads {
-  static constexpr int n = 1;
-};
-template <>
-struct FragReads<ColDirect> {
-  static constexpr int n = 2;
-};
-
 struct Frags {
-  uint4 a[kTM], b[kTN];
+  u32x4_t a[kTM], b[kTN];
 };
 
+// Wait for this wave's outstanding LDS reads; tying the fragment registers
+// keeps every use of them after the wait.
+__device__ __forceinline__ void lds_wait_frags(Frags& f) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]),
+                 "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3]));
+}
+
+// The j-th LDS read of a step's fragments: A blocks first, then B blocks.
 template <class LA, class LB>
-__device__ __forceinline__ void read_frags(Frags& f, const lds_t* A, const lds_t* B, int wm, int wn,
-                                           int s, int lane) {
-#pragma unroll
-  for (int a = 0; a < kTM; ++a) f.a[a] = LA::frag(A, wm * kWTM + a * 32, s, lane);
-#pragma unroll
-  for (int b = 0; b < kTN; ++b) f.b[b] = LB::frag(B, wn * kWTN + b * 32, s, lane);
-}
-
-template <bool BF16>
-__device__ __forceinline__ void mma_step(Acc& acc, const Frags& f) {
-#pragma unroll
-  for (int a = 0; a < kTM; ++a)
-#pragma unroll
-    for (int b = 0; b < kTN; ++b) mma<BF16>(acc[a][b], f.a[a], f.b[b]);
-}
-
-// Ask the scheduler to interleave the next step's LDS reads with this step's
-// MFMAs: one MFMA, one read, ..., then the remaining MFMAs.
-template <bool BF16, int NREADS>
-__device__ __forceinline__ void interleave_step() {
-  constexpr int kMfma = kTM * kTN * (BF16 ? 1 : 4);
-  constexpr int kPairs = NREADS < kMfma ? NREADS : kMfma;
-#pragma unroll
-  for (int j = 0; j < kPairs; ++j) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+__device__ __forceinline__ void issue_read(int j, Frags& f, const lds_t* A, const lds_t* B, int wm,
+                                           int wn, int s, int lane) {
+  constexpr int RA = LA::kReads, RB = LB::kReads;
+  if (j < kTM * RA) {
+    const int a = j / RA, h = j % RA;
+    LA::frag_part(f.a[a], A, wm * kWTM + a * 32, s, h, lane);
+  } else {
+    const int jb = j - kTM * RA;
+    const int b = jb / RB, h = jb % RB;
+    LB::frag_part(f.b[b], B, wn * kWTN + b * 32, s, h, lane);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kPairs, 0);
+}
+
+// One contraction step: the 16 MFMA block products on `cur`, with the reads
+// of the fragments `nxt` for step s interleaved one per MFMA. The order is
+// pinned with scheduling barriers.
+template <bool BF16, class LA, class LB>
+__device__ __forceinline__ void step(Acc& acc, const Frags& cur, Frags& nxt, const lds_t* A,
+                                     const lds_t* B, int wm, int wn, int s, int lane) {
+  constexpr int kReads = kTM * LA::kReads + kTN * LB::kReads;
+  static_assert(kReads <= kTM * kTN, "one read per MFMA slot");
+#pragma unroll
+  for (int j = 0; j < kTM * kTN; ++j) {
+    mma<BF16>(acc[j / kTN][j % kTN], cur.a[j / kTN], cur.b[j % kTN]);
+    if (j < kReads) issue_read<LA, LB>(j, nxt, A, B, wm, wn, s, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// All reads of one step's fragments, for the pipeline prologue.
+template <class LA, class LB>
+__device__ __forceinline__ void read_all(Frags& f, const lds_t* A, const lds_t* B, int wm, int wn,
+                                         int s, int lane) {
+  constexpr int kReads = kTM * LA::kReads + kTN * LB::kReads;
+#pragma unroll
+  for (int j = 0; j < kReads; ++j) issue_read<LA, LB>(j, f, A, B, wm, wn, s, lane);
+}
+
+// Workgroup barrier without a memory fence. __syncthreads() also fences,
+// which waits for every outstanding LDS-DMA of the wave (vmcnt(0)) and so
+// would drain the whole pipeline; here the waits are explicit (wait_vmem_le,
+// wait_lds) and the signal fences only stop the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void block_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wait until at most N LDS-DMA / global loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
 // acc = Σ over stages [kt0, kt1) of A-tile(a0) · B-tile(b0)ᵀ, where A rows are
 // the M index and B rows the N index of the 256×256 tile; kt1 > kt0. Ends
 // with a barrier, so the caller may reuse `smem` at once.
 //
-// Per stage (4 contraction steps of 16 bytes per lane): the DMA of the next
-// stage is issued first; each step's MFMAs run while the next step's
-// fragments are read; before the last step every wave waits for its DMA and
-// its LDS reads and meets the others at the one barrier of the stage, then
-// reads the next stage's first fragments under the last step's MFMAs. The
-// last stage is peeled so the steady-state loop has no branches.
+// LDS holds a ring of kStages stages. Every iteration issues the DMA of stage
+// kt + kStages - 1 (past the end it fetches zeros into a slot nobody reads),
+// so exactly (kStages - 2) stages' worth of DMA may stay in flight when the
+// wave waits for stage kt + 1: the vmcnt threshold is a constant. Each step's
+// MFMAs run while the next step's fragments are read; before the last step
+// every wave waits for its DMA and its LDS reads and meets the others at the
+// one barrier of the iteration, then reads the next stage's first fragments
+// under the last step's MFMAs.
 template <bool BF16, class LA, class OA, class LB, class OB>
 __device__ __forceinline__ void gemm_tile(Acc& acc, const OA& oa, int a0, const OB& ob, int b0,
                                           int kt0, int kt1, lds_t* smem) {
-  constexpr int kReads = kTM * FragReads<LA>::n + kTN * FragReads<LB>::n;
+  constexpr int kDma = LA::kDma + LB::kDma;
+  static_assert(kSteps % 2 == 0, "steps alternate between two fragment sets");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % kWM, wn = wave / kWM;
@@ -299,62 +365,51 @@ __device__ __forceinline__ void gemm_tile(Acc& acc, const OA& oa, int a0, const 
 
   LA la;
   LB lb;
-  lds_t* const A0 = smem;
-  lds_t* const B0 = smem + kOpBytes;
-  lds_t* const A1 = smem + 2 * kOpBytes;
-  lds_t* const B1 = smem + 3 * kOpBytes;
-  la.fetch(oa, a0, kt0, A0, wave, lane, tid);
-  lb.fetch(ob, b0, kt0, B0, wave, lane, tid);
-  la.commit(A0, tid);
-  lb.commit(B0, tid);
-  wait_vmem();
-  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kStages - 1; ++j) {
+    lds_t* const st = smem + j * kStageBytes;
+    la.fetch(oa, a0, kt0 + j, st, wave, lane, tid);
+    lb.fetch(ob, b0, kt0 + j, st + kOpBytes, wave, lane, tid);
+    la.commit(st, tid);
+    lb.commit(st + kOpBytes, tid);
+  }
+  wait_vmem_le<(kStages - 2) * kDma>();
+  wait_lds();
+  block_barrier();
 
   Frags f0, f1;
-  read_frags<LA, LB>(f0, A0, B0, wm, wn, 0, lane);
-  int kt = kt0;
-  for (; kt + 1 < kt1; ++kt) {
-    const bool odd = (kt - kt0) & 1;
-    const lds_t* const Ac = odd ? A1 : A0;
-    const lds_t* const Bc = odd ? B1 : B0;
-    lds_t* const An = odd ? A0 : A1;
-    lds_t* const Bn = odd ? B0 : B1;
-    la.fetch(oa, a0, kt + 1, An, wave, lane, tid);
-    lb.fetch(ob, b0, kt + 1, Bn, wave, lane, tid);
-    read_frags<LA, LB>(f1, Ac, Bc, wm, wn, 1, lane);
-    mma_step<BF16>(acc, f0);
-    interleave_step<BF16, kReads>();
-    read_frags<LA, LB>(f0, Ac, Bc, wm, wn, 2, lane);
-    mma_step<BF16>(acc, f1);
-    interleave_step<BF16, kReads>();
-    read_frags<LA, LB>(f1, Ac, Bc, wm, wn, 3, lane);
-    mma_step<BF16>(acc, f0);
-    interleave_step<BF16, kReads>();
-    la.commit(An, tid);
-    lb.commit(Bn, tid);
-    wait_vmem();
-    wait_lds();
-    __syncthreads();  // next stage landed everywhere; nobody reads this stage any more
-    read_frags<LA, LB>(f0, An, Bn, wm, wn, 0, lane);
-    mma_step<BF16>(acc, f1);
-    interleave_step<BF16, kReads>();
+  read_all<LA, LB>(f0, smem, smem + kOpBytes, wm, wn, 0, lane);
+  int slot = 0;  // ring slot of stage kt
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const lds_t* const cur = smem + slot * kStageBytes;
+    const int next_slot = slot + 1 == kStages ? 0 : slot + 1;
+    const int fill_slot = slot == 0 ? kStages - 1 : slot - 1;  // held stage kt - 1
+    lds_t* const fill = smem + fill_slot * kStageBytes;
+    la.fetch(oa, a0, kt + kStages - 1, fill, wave, lane, tid);
+    lb.fetch(ob, b0, kt + kStages - 1, fill + kOpBytes, wave, lane, tid);
+    lds_wait_frags(f0);
+#pragma unroll
+    for (int st = 0; st + 1 < kSteps; ++st) {
+      if (st % 2 == 0) {
+        step<BF16, LA, LB>(acc, f0, f1, cur, cur + kOpBytes, wm, wn, st + 1, lane);
+        if (st + 2 < kSteps) lds_wait_frags(f1);
+      } else {
+        step<BF16, LA, LB>(acc, f1, f0, cur, cur + kOpBytes, wm, wn, st + 1, lane);
+        lds_wait_frags(f0);
+      }
+    }
+    la.commit(fill, tid);
+    lb.commit(fill + kOpBytes, tid);
+    wait_vmem_le<(kStages - 2) * kDma>();
+    lds_wait_frags(f1);
+    block_barrier();  // stage kt+1 landed everywhere; nobody reads stage kt any more
+    const lds_t* const nxt = smem + next_slot * kStageBytes;
+    step<BF16, LA, LB>(acc, f1, f0, nxt, nxt + kOpBytes, wm, wn, 0, lane);
+    slot = next_slot;
   }
-  {
-    const bool odd = (kt - kt0) & 1;
-    const lds_t* const Ac = odd ? A1 : A0;
-    const lds_t* const Bc = odd ? B1 : B0;
-    read_frags<LA, LB>(f1, Ac, Bc, wm, wn, 1, lane);
-    mma_step<BF16>(acc, f0);
-    interleave_step<BF16, kReads>();
-    read_frags<LA, LB>(f0, Ac, Bc, wm, wn, 2, lane);
-    mma_step<BF16>(acc, f1);
-    interleave_step<BF16, kReads>();
-    read_frags<LA, LB>(f1, Ac, Bc, wm, wn, 3, lane);
-    mma_step<BF16>(acc, f0);
-    interleave_step<BF16, kReads>();
-    mma_step<BF16>(acc, f1);
-  }
-  __syncthreads();
+  wait_vmem_le<0>();
+  wait_lds();
+  block_barrier();
 }
 
 // Position of accumulator element (a, b, i) of `lane` inside the 256×256
@@ -379,17 +434,6 @@ __device__ __forceinline__ Owner acc_owner(int wr, int wc) {
   o.blk = (wr >> 5) * kTN + (wc >> 5);
   o.reg = (rr & 3) + 4 * (rr >> 3);
   return o;
-}
-
-// Apply f(block, register-select) to the one accumulator block `blk`
-// (wave-uniform): a uniform branch per block, a 16-way select inside it.
-template <class F>
-__device__ __forceinline__ void acc_visit(Acc& acc, int blk, F&& f) {
-#pragma unroll
-  for (int a = 0; a < kTM; ++a)
-#pragma unroll
-    for (int b = 0; b < kTN; ++b)
-      if (blk == a * kTN + b) f(acc[a][b]);
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup i goes to

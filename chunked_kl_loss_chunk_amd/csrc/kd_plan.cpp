@@ -41,8 +41,8 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
   q.nVt = q.V_pad / kTileN;
   q.nMt = q.C_pad / kTileM;
   q.nb = q.nMt * q.nVt;
-  q.kt_d = cdiv(d * es, kStageBytes);
-  q.kt_v = cdiv(q.V_pad * es, kStageBytes);
+  q.kt_d = cdiv(d * es, kStageRowBytes);
+  q.kt_v = cdiv(q.V_pad * es, kStageRowBytes);
   if (q.C * K > (int64_t(1) << 30) || q.nb > (int64_t(1) << 30)) return KD_ERR_UNSUPPORTED;
 
   // dH = dlogits · W has a short output (C × d) and a long contraction (V):

@@ -13,7 +13,7 @@ namespace kd {
 constexpr int kTileM = 256;  // tokens
 constexpr int kTileN = 256;  // vocabulary
 // Bytes of the contraction dimension staged per LDS row and pipeline stage.
-constexpr int kStageBytes = 128;
+constexpr int kStageRowBytes = 64;
 // Packed hit record: token-in-tile (8 bits), vocab-in-tile (10 bits), k (14 bits).
 constexpr int64_t kMaxK = (1 << 14) - 1;
 // Upper bound on the dH split-K factor.
@@ -31,7 +31,7 @@ struct Plan {
   int64_t nVt;    // vocabulary tiles
   int64_t nMt;    // row tiles per chunk
   int64_t nb;     // hit buckets per chunk = nMt * nVt
-  int64_t kt_d;   // stages along d   (d * es / kStageBytes, rounded up)
+  int64_t kt_d;   // stages along d   (d * es / kStageRowBytes, rounded up)
   int64_t kt_v;   // stages along V_pad
   int dh_splits;  // split-K factor of the dH contraction
   // byte offsets inside the workspace (all 256-byte aligned)
