@@ -438,11 +438,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs a) {
       }
   }
 
-  // Store: four consecutive vocabulary entries of one token per lane.
+  // Store: four consecutive vocabulary entries of one token per lane. Only
+  // the chunk's own rows are written (the next chunk's rows follow them).
   T* dl = reinterpret_cast<T*>(a.dl);
 #pragma unroll
   for (int b = 0; b < kTN; ++b) {
     const int64_t tok = t_base + acc_col(wn, b, lane);
+    if (tok >= a.rows) continue;
 #pragma unroll
     for (int t = 0; t < kTM; ++t)
 #pragma unroll
@@ -590,6 +592,38 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dw(DwArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % kWM, wn = wave / kWM;
+  // Each lane owns, per block, four consecutive d of one vocabulary row: one
+  // float4 of dW. Full tiles take a branch-free path that issues a whole
+  // block column's 16 loads before the first add, so the read-modify-write
+  // costs four memory round trips per tile, not 64.
+  const bool full = v_base + kBN <= a.V && d_base + kBM <= a.d;
+  if (full) {
+#pragma unroll
+    for (int b = 0; b < kTN; ++b) {
+      float* row = a.dW + int64_t(v_base + acc_col(wn, b, lane)) * a.d + d_base;
+      float4 old[kTM * 4];
+      if (a.beta) {
+#pragma unroll
+        for (int t = 0; t < kTM; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            old[t * 4 + q] = *reinterpret_cast<const float4*>(row + acc_row(wm, t, 4 * q, lane));
+      } else {
+#pragma unroll
+        for (int i = 0; i < kTM * 4; ++i) old[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int t = 0; t < kTM; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 y = old[t * 4 + q];
+          *reinterpret_cast<float4*>(row + acc_row(wm, t, 4 * q, lane)) =
+              make_float4(acc[t][b][4 * q] + y.x, acc[t][b][4 * q + 1] + y.y,
+                          acc[t][b][4 * q + 2] + y.z, acc[t][b][4 * q + 3] + y.w);
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < kTN; ++b) {
     const int v = v_base + acc_col(wn, b, lane);
@@ -742,11 +776,17 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
   const int k_per_stage = kLdsRow / p.es;
   auto dh_kernel = k_bwd_dh<BF16, ColLoad<BF16>>;
   auto dw_kernel = k_bwd_dw<BF16, ColLoad<BF16>>;
+  const int64_t dl_ld_bytes = p.V_pad * p.es;
+  int64_t win_r0 = 0;   // first row of the current dW window
+  int win_chunks = 0;   // chunks of the window held in the dlogits scratch
+  bool dw_written = accumulate != 0;
   for (int64_t r0 = 0; r0 < p.N; r0 += p.C) {
     const int rows = int(p.N - r0 < p.C ? p.N - r0 : p.C);
     launch_prep(p, ws, idx, logp, r0, rows, st);
     const char* Hc = static_cast<const char*>(H) + r0 * row_bytes;
     const int tiles_t = int(cdiv(rows, kBN));
+    if (win_chunks == 0) win_r0 = r0;
+    char* const dl_c = ws.at<char>(p.off_dl) + int64_t(win_chunks) * p.C * dl_ld_bytes;
 
     DlArgs a;
     a.W = RowOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
@@ -762,18 +802,17 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
     a.lse = lse + r0;
     a.rowS = ws.at<float>(p.off_rowS);
     a.grad = grad;
-    a.dl = ws.at<char>(p.off_dl);
+    a.dl = dl_c;
     a.ld_dl = p.V_pad;
     timed(KD_KERNEL_BWD_DLOGITS, st, [&] {
       hipLaunchKernelGGL(k_bwd_dlogits<BF16>, dim3(a.tiles_t * a.tiles_v), dim3(kThreads), 0, st,
                          a);
     });
 
-    const int64_t dl_ld_bytes = p.V_pad * p.es;
     if (dH) {
       DhArgs h;
       h.W = ColOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
-      h.dl = RowOp{ws.at<char>(p.off_dl), dl_ld_bytes, rows, int(dl_ld_bytes)};
+      h.dl = RowOp{dl_c, dl_ld_bytes, rows, int(dl_ld_bytes)};
       h.tiles_t = tiles_t;
       h.tiles_d = int(cdiv(p.d, kBM));
       h.splits = p.dh_splits;
@@ -796,21 +835,28 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
         });
       }
     }
-    if (dW) {
+    ++win_chunks;
+    const bool last = r0 + rows >= p.N;
+    if (dW && (win_chunks == p.dw_window || last)) {
+      // dW (+)= dlᵀ H over the window's rows, in chunk order.
+      const int krows = int(r0 + rows - win_r0);
       DwArgs w;
-      w.H = ColOp{Hc, row_bytes, rows, int(row_bytes)};
-      w.dl = ColOp{ws.at<char>(p.off_dl), dl_ld_bytes, rows, int(dl_ld_bytes)};
+      w.H = ColOp{static_cast<const char*>(H) + win_r0 * row_bytes, row_bytes, krows,
+                  int(row_bytes)};
+      w.dl = ColOp{ws.at<char>(p.off_dl), dl_ld_bytes, krows, int(dl_ld_bytes)};
       w.tiles_d = int(cdiv(p.d, kBM));
       w.tiles_v = int(cdiv(p.V, kBN));
-      w.kt = int(cdiv(rows, k_per_stage));
+      w.kt = int(cdiv(krows, k_per_stage));
       w.V = int(p.V);
       w.d = int(p.d);
       w.dW = dW;
-      w.beta = (accumulate || r0 > 0) ? 1 : 0;
+      w.beta = dw_written ? 1 : 0;
       timed(KD_KERNEL_BWD_DW, st, [&] {
         hipLaunchKernelGGL(dw_kernel, dim3(w.tiles_d * w.tiles_v), dim3(kThreads), 0, st, w);
       });
+      dw_written = true;
     }
+    if (win_chunks == p.dw_window) win_chunks = 0;
   }
   return launch_status();
 }

@@ -53,6 +53,8 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
   if (splits > q.kt_v) splits = q.kt_v;
   if (splits < 1) splits = 1;
   q.dh_splits = static_cast<int>(splits);
+  const int64_t n_chunks = N > 0 ? cdiv(N, q.C) : 1;
+  q.dw_window = static_cast<int>(n_chunks < kDwWindow ? n_chunks : kDwWindow);
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -72,7 +74,9 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
     q.off_dl = q.off_dhpart = 0;
   } else {
     q.off_zhit = q.off_part = q.off_loss = 0;
-    q.off_dl = take(size_t(es) * size_t(q.C_pad) * size_t(q.V_pad));
+    // The window's chunks are packed back to back ([window·C][V_pad]); the
+    // last tile of the last chunk may read (never write) up to C_pad rows.
+    q.off_dl = take(size_t(es) * size_t((q.dw_window - 1) * q.C + q.C_pad) * size_t(q.V_pad));
     q.off_dhpart = q.dh_splits > 1 ? take(sizeof(float) * size_t(q.dh_splits) * size_t(q.C_pad) *
                                           size_t(d))
                                     : 0;

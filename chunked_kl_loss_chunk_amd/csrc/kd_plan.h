@@ -20,6 +20,10 @@ constexpr int64_t kMaxK = (1 << 14) - 1;
 constexpr int kMaxDhSplits = 32;
 // Target number of dH workgroups per chunk (three waves of the 256 CUs).
 constexpr int kDhTargetTiles = 768;
+// dW is contracted over this many consecutive chunks at once: its fp32
+// read-modify-write of V×d happens once per window instead of once per chunk,
+// for a backward scratch of window × chunk × V dlogits.
+constexpr int kDwWindow = 2;
 
 struct Plan {
   int64_t N, d, V, K, chunk;
@@ -34,6 +38,7 @@ struct Plan {
   int64_t kt_d;   // stages along d   (d * es / kStageRowBytes, rounded up)
   int64_t kt_v;   // stages along V_pad
   int dh_splits;  // split-K factor of the dH contraction
+  int dw_window;  // chunks whose dlogits are held before one dW contraction
   // byte offsets inside the workspace (all 256-byte aligned)
   size_t off_counts, off_offsets, off_recs, off_rowS, off_zhit, off_part, off_loss, off_flag;
   size_t off_dl, off_dhpart;
