@@ -41,6 +41,7 @@ namespace kd {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <bool BF16>
 struct Elt;
@@ -248,28 +249,28 @@ __device__ __forceinline__ uint64_t hits_mine(const TileHits& t, const uint2& r,
   return __ballot(base + lane < t.n && unsigned(wr) < unsigned(kWTM) && unsigned(wc) < unsigned(kWTN));
 }
 
-// Accumulator element `reg` of block `blk` (both wave-uniform).
-__device__ __forceinline__ float acc_pick(const Acc& acc, int blk, int reg) {
-  float v = 0.f;
+// Any lane can read any accumulator element of its wave once one 128×32
+// column block (b) is staged in a wave-private LDS region as [col][row] fp32
+// with a padded column stride (consecutive lanes write different columns;
+// the pad spreads them over the banks). LDS operations of one wave execute
+// in order, so the wave reads its own writes without a barrier.
+constexpr int kColStride = kWTM + 4;                       // floats per staged column
+constexpr int kStageBlockBytes = 32 * kColStride * 4;       // one wave's region
+typedef __attribute__((address_space(3))) float lds_f32;
+
+__device__ __forceinline__ void stage_block_column(const Acc& acc, int b, lds_f32* region, int lane) {
 #pragma unroll
-  for (int a = 0; a < kTM; ++a)
+  for (int t = 0; t < kTM; ++t)
 #pragma unroll
-    for (int b = 0; b < kTN; ++b)
-      if (blk == a * kTN + b) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v = (i == reg) ? acc[a][b][i] : v;
-      }
-  return v;
+    for (int q = 0; q < 4; ++q) {
+      const int row = t * 32 + 8 * q + 4 * (lane >> 5);
+      *reinterpret_cast<__attribute__((address_space(3))) f32x4_t*>(region + (lane & 31) * kColStride + row) =
+          f32x4_t{acc[t][b][4 * q], acc[t][b][4 * q + 1], acc[t][b][4 * q + 2], acc[t][b][4 * q + 3]};
+    }
 }
-__device__ __forceinline__ void acc_sub_at(Acc& acc, int blk, int reg, float x) {
-#pragma unroll
-  for (int a = 0; a < kTM; ++a)
-#pragma unroll
-    for (int b = 0; b < kTN; ++b)
-      if (blk == a * kTN + b) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[a][b][i] = (i == reg) ? acc[a][b][i] - x : acc[a][b][i];
-      }
+
+__device__ __forceinline__ float staged_at(const lds_f32* region, int wr, int wc) {
+  return region[(wc & 31) * kColStride + wr];
 }
 
 template <bool BF16>
@@ -288,48 +289,74 @@ __global__ __launch_bounds__(kThreads) void k_fwd_logits(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % kWM, wn = wave / kWM;
 
-  // z at the cached teacher ids that fall in this tile.
   const TileHits hits = hits_begin(a.offsets, a.recs, tt * a.nVt + vt, lane);
-  for (int base = 0; base < hits.n; base += 64) {
-    const uint2 r = hits_load(hits, base, lane);
-    uint64_t mask = hits_mine(hits, r, base, wm, wn, lane);
-    while (mask) {
-      const int j = __builtin_ctzll(mask);
-      mask &= mask - 1;
-      const uint32_t x = __builtin_amdgcn_readlane(r.x, j);
-      const int tok = int(x & 255u), voc = int((x >> 8) & 1023u), k = int(x >> 18);
-      const Owner o = acc_owner(voc - wm * kWTM, tok - wn * kWTN);
-      const float z = acc_pick(acc, o.blk, o.reg);
-      if (lane == o.lane) a.zhit[int64_t(t_base + tok) * a.K + k] = z;
-    }
-  }
 
   // Per token: max and Σexp over this tile's valid vocabulary rows.
   const int vlim = a.V - (v_base + wm * kWTM);  // rows of this wave below vlim are valid
+  const bool full = vlim >= kWTM;
   float2* red = reinterpret_cast<float2*>(smem_raw);  // [kWM][kBN]
 #pragma unroll
   for (int b = 0; b < kTN; ++b) {
     float m = kNegInf;
+    if (full) {
 #pragma unroll
-    for (int t = 0; t < kTM; ++t)
+      for (int t = 0; t < kTM; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = t * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        m = r < vlim ? fmaxf(m, acc[t][b][i]) : m;
-      }
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[t][b][i]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kTM; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = t * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          m = r < vlim ? fmaxf(m, acc[t][b][i]) : m;
+        }
+    }
     m = fmaxf(m, __shfl_xor(m, 32));
     const float ms = m == kNegInf ? 0.f : m;
     float s = 0.f;
+    if (full) {
 #pragma unroll
-    for (int t = 0; t < kTM; ++t)
+      for (int t = 0; t < kTM; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = t * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        s += r < vlim ? __expf(acc[t][b][i] - ms) : 0.f;
-      }
+        for (int i = 0; i < 16; ++i) s += __expf(acc[t][b][i] - ms);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kTM; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = t * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          s += r < vlim ? __expf(acc[t][b][i] - ms) : 0.f;
+        }
+    }
     s += __shfl_xor(s, 32);
     if (lane < 32) red[wm * kBN + acc_col(wn, b, lane)] = make_float2(m, s);
   }
+
+  // z at the cached teacher ids that fall in this tile, one column block at a time.
+  lds_f32* region = reinterpret_cast<lds_f32*>(smem + kWM * kBN * sizeof(float2)) +
+                    wave * (kStageBlockBytes / 4);
+  for (int base = 0; base < hits.n; base += 64) {
+    const uint2 r = hits_load(hits, base, lane);
+    const uint64_t mine = hits_mine(hits, r, base, wm, wn, lane);
+    if (mine == 0) continue;
+#pragma unroll
+    for (int b = 0; b < kTN; ++b) {
+      const int wc_lane = int(r.x & 255u) - wn * kWTN;
+      uint64_t mask = mine & __ballot((wc_lane >> 5) == b);
+      if (mask == 0) continue;
+      stage_block_column(acc, b, region, lane);
+      while (mask) {
+        const int j = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        const uint32_t x = __builtin_amdgcn_readlane(r.x, j);
+        const int tok = int(x & 255u), voc = int((x >> 8) & 1023u), k = int(x >> 18);
+        const float z = staged_at(region, voc - wm * kWTM, tok - wn * kWTN);
+        if (lane == 0) a.zhit[int64_t(t_base + tok) * a.K + k] = z;
+      }
+    }
+  }
+
   __syncthreads();
   if (t_base + tid < a.rows) {
     float m = red[tid].x, s = red[tid].y;
@@ -423,19 +450,29 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs a) {
   const int vlim = a.V - (v_base + wm * kWTM);
   const TileHits hits = hits_begin(a.offsets, a.recs, tt * a.nVt + vt, lane);
 
+  // dl = g S_r exp(z − lse_r); tokens past the chunk give 0 (gs = 0), and so
+  // do vocabulary rows past V (only in the last vocabulary tile).
+  const bool full = vlim >= kWTM;
 #pragma unroll
   for (int b = 0; b < kTN; ++b) {
     const int tok = t_base + acc_col(wn, b, lane);
     const bool tok_ok = tok < a.rows;
     const float l = tok_ok ? a.lse[tok] : 0.f;
     const float gs = tok_ok ? g * a.rowS[tok] : 0.f;
+    if (full) {
 #pragma unroll
-    for (int t = 0; t < kTM; ++t)
+      for (int t = 0; t < kTM; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = t * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        acc[t][b][i] = (tok_ok && r < vlim) ? gs * __expf(acc[t][b][i] - l) : 0.f;
-      }
+        for (int i = 0; i < 16; ++i) acc[t][b][i] = gs * __expf(acc[t][b][i] - l);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kTM; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = t * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          acc[t][b][i] = r < vlim ? gs * __expf(acc[t][b][i] - l) : 0.f;
+        }
+    }
   }
 
   // Store: four consecutive vocabulary entries of one token per lane. Only
@@ -465,18 +502,27 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs a) {
   // At the cached ids of this tile the value is S_r q − p, not S_r q: the
   // lane that owns the element stores the corrected value over the one it
   // just wrote (same thread, same address: the later store wins).
+  lds_f32* region = reinterpret_cast<lds_f32*>(smem) + wave * (kStageBlockBytes / 4);
   for (int base = 0; base < hits.n; base += 64) {
     const uint2 r = hits_load(hits, base, lane);
-    uint64_t mask = hits_mine(hits, r, base, wm, wn, lane);
-    while (mask) {
-      const int j = __builtin_ctzll(mask);
-      mask &= mask - 1;
-      const uint32_t x = __builtin_amdgcn_readlane(r.x, j);
-      const float p = __uint_as_float(__builtin_amdgcn_readlane(r.y, j));
-      const int tok = int(x & 255u), voc = int((x >> 8) & 1023u);
-      const Owner o = acc_owner(voc - wm * kWTM, tok - wn * kWTN);
-      const float v = acc_pick(acc, o.blk, o.reg) - g * p;
-      if (lane == o.lane) dl[int64_t(t_base + tok) * a.ld_dl + v_base + voc] = T(v);
+    const uint64_t mine = hits_mine(hits, r, base, wm, wn, lane);
+    if (mine == 0) continue;
+#pragma unroll
+    for (int b = 0; b < kTN; ++b) {
+      const int wc_lane = int(r.x & 255u) - wn * kWTN;
+      uint64_t mask = mine & __ballot((wc_lane >> 5) == b);
+      if (mask == 0) continue;
+      stage_block_column(acc, b, region, lane);
+      while (mask) {
+        const int j = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        const uint32_t x = __builtin_amdgcn_readlane(r.x, j);
+        const float p = __uint_as_float(__builtin_amdgcn_readlane(r.y, j));
+        const int tok = int(x & 255u), voc = int((x >> 8) & 1023u);
+        const int wr = voc - wm * kWTM, wc = tok - wn * kWTN;
+        const float v = staged_at(region, wr, wc) - g * p;
+        if (lane == acc_owner(wr, wc).lane) dl[int64_t(t_base + tok) * a.ld_dl + v_base + voc] = T(v);
+      }
     }
   }
 }
