@@ -153,13 +153,14 @@ def fused_kl_reference(H, W, idx, logp, grad: float = 1.0) -> dict:
     }
 
 
-def rows_reference(H, W, idx, logp, rows, grad: float = 1.0) -> dict:
+def rows_reference(H, W, idx, logp, rows, grad: float = 1.0, with_dh: bool = True) -> dict:
     """The same definition evaluated on a subset of rows.
 
     Every quantity except dW depends on its own row only, so loss_tok, lse,
     dlogits and dH of the selected rows can be checked one by one at sizes
-    where the full dense grid would not fit. ``W`` may be passed already
-    upcast (a float64 array) to avoid repeating the conversion.
+    where the full dense grid would not fit; dW is the sum over row blocks of
+    dlogitsᵀ H. ``W`` may be passed already upcast (a float64 array) to avoid
+    repeating the conversion; ``with_dh=False`` skips the dH product.
     """
     rows = np.asarray(rows, dtype=np.int64)
     Hs = to_f64(H[rows] if not hasattr(H, "detach") else H[rows.tolist()])
@@ -171,4 +172,7 @@ def rows_reference(H, W, idx, logp, rows, grad: float = 1.0) -> dict:
     _, lse, logq = student_log_softmax(Hs, W64)
     loss_tok = kl_rows(P, logq)
     G = kl_grad_logits(P, logq, grad)
-    return {"rows": rows, "loss_tok": loss_tok, "lse": lse, "dlogits": G, "dH": G @ W64}
+    out = {"rows": rows, "loss_tok": loss_tok, "lse": lse, "dlogits": G}
+    if with_dh:
+        out["dH"] = G @ W64
+    return out

@@ -193,3 +193,68 @@ def test_autograd_function(kd):
     assert Hd.grad.dtype == torch.bfloat16 and Wd.grad.dtype == torch.bfloat16
     assert max_norm_err(Hd.grad.double().cpu().numpy(), ref["dH"]) < 2e-2
     assert max_norm_err(Wd.grad.double().cpu().numpy(), ref["dW"]) < 2e-2
+
+
+# --------------------------------------------------------------------------
+# full size, in the launch configuration bench.py times (8K-token head)
+# --------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def head8k(kd):
+    cfg = workload.config(3)
+    H, W, idx, logp = workload.make_inputs(cfg, teacher_device="cuda")
+    Hd, Wd, id_, lp = _to_dev(H, W, idx, logp)
+    loss_sum, loss_tok, lse = kd.kl_forward(Hd, Wd, id_, lp, cfg.chunk)
+    g = torch.ones(1, dtype=torch.float32, device=Hd.device)
+    dH, dW = kd.kl_backward(Hd, Wd, id_, lp, lse, g, cfg.chunk)
+    torch.cuda.synchronize()
+    out = {"loss": float(loss_sum.item()), "loss_tok": loss_tok.double().cpu().numpy(),
+           "lse": lse.double().cpu().numpy(), "dH": dH.double().cpu().numpy(),
+           "dW": dW.double().cpu().numpy()}
+    del Hd, Wd, id_, lp, dH, dW, lse, loss_tok
+    torch.cuda.empty_cache()
+    return cfg, (H, W, idx, logp), out
+
+
+def test_full_size_sampled_rows(head8k):
+    cfg, (H, W, idx, logp), got = head8k
+    rng = np.random.default_rng(31)
+    rows = sorted(set([0, 1, 255, 256, 1023, 1024, 4097, cfg.N - 1]) |
+                  set(rng.integers(0, cfg.N, 8).tolist()))
+    W64 = oracle.to_f64(W)
+    ref = oracle.rows_reference(H, W64, idx, logp, rows)
+    assert rel_err(got["loss_tok"][rows], ref["loss_tok"]) < 2e-3
+    assert rel_err(got["lse"][rows], ref["lse"]) < 2e-3
+    assert max_norm_err(got["dH"][rows], ref["dH"]) < 2e-2
+    # the reported sum is the fixed-order sum of the per-token losses
+    assert abs(got["loss"] - got["loss_tok"].sum()) <= 1e-5 * abs(got["loss_tok"].sum())
+
+
+def test_full_size_gradient_identities(head8k):
+    """Properties that hold at any size: every dlogits row sums to zero, so every
+    column of dW sums to zero; and <dW, W> = <dH, H> = Σ G∘Z."""
+    cfg, (H, W, idx, logp), got = head8k
+    dW, dH = got["dW"], got["dH"]
+    colsum = np.abs(dW.sum(axis=0)).max()
+    assert colsum < 1e-3 * np.abs(dW).max() * np.sqrt(cfg.V)
+    a = float((dW * W.double().numpy()).sum())
+    b = float((dH * H.double().numpy()).sum())
+    assert abs(a - b) < 2e-2 * max(abs(a), abs(b), 1e-12)
+
+
+@pytest.mark.timeout(1200)
+def test_full_size_sampled_dw_rows(head8k):
+    """dW rows (vocabulary entries) against the oracle's dlogits assembled
+    over all 8192 rows in blocks of one chunk."""
+    cfg, (H, W, idx, logp), got = head8k
+    rng = np.random.default_rng(32)
+    hit_ids = np.unique(idx[:64].numpy().reshape(-1))
+    J = np.unique(np.concatenate([hit_ids[:8], rng.integers(0, cfg.V, 8), [0, cfg.V - 1]]))
+    W64 = oracle.to_f64(W)
+    H64 = oracle.to_f64(H)
+    ref = np.zeros((len(J), cfg.d))
+    for r0 in range(0, cfg.N, cfg.chunk):
+        rows = np.arange(r0, min(cfg.N, r0 + cfg.chunk))
+        part = oracle.rows_reference(H, W64, idx, logp, rows, with_dh=False)
+        ref += part["dlogits"][:, J].T @ H64[rows]
+        del part
+    assert max_norm_err(got["dW"][J], ref) < 2e-2

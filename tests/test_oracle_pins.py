@@ -225,6 +225,20 @@ def test_rows_reference_matches_full():
         np.testing.assert_allclose(part[k], full[k][rows], rtol=1e-14, atol=1e-16)
 
 
+def test_row_blocks_assemble_dw():
+    """dW is the sum over row blocks of dlogitsᵀ H (the full-size GPU check relies on it)."""
+    rng = np.random.default_rng(26)
+    H, W, idx, logp = _rand_case(rng, 20, 5, 40, 4)
+    full = oracle.fused_kl_reference(H, W, idx, logp, grad=0.8)
+    dW = np.zeros_like(full["dW"])
+    for r0 in range(0, 20, 6):
+        rows = list(range(r0, min(20, r0 + 6)))
+        part = oracle.rows_reference(H, W, idx, logp, rows, grad=0.8, with_dh=False)
+        assert "dH" not in part
+        dW += part["dlogits"].T @ H[rows]
+    np.testing.assert_allclose(dW, full["dW"], rtol=1e-13, atol=1e-15)
+
+
 def test_invalid_cache_rejected():
     with pytest.raises(ValueError):
         ko.teacher_grid(np.array([[0, 0]]), np.zeros((1, 2)), 5)
