@@ -16,7 +16,7 @@
 // accumulators per lane). The contraction is staged through LDS 64 bytes per
 // row at a time (32 bf16 or 16 fp32) in a ring of four stages (128 KiB of
 // LDS), three of them in flight while the fourth is consumed. Operands are
-// copied global→LDS by the LDS-DMA path (global_load_lds, 16 bytes per lane,
+// copied global→LDS by the LDS-DMA path (buffer_load ... lds, 16 bytes per lane,
 // no VGPRs), in one of two layouts:
 //
 //   RowDirect  operand stored [rows][K] (K contiguous). LDS [256 rows][64 B],
@@ -30,8 +30,9 @@
 //              four K-rows per thread are transposed in registers on their way
 //              into the row layout.
 //
-// Out-of-range rows, columns and K-tails are fetched from a 64-byte block of
-// zeros, so partial tiles need no special cases.
+// Operands are read through buffer resources whose record counts end at the
+// operand's last valid row (or K-row): out-of-range rows, columns and K-tails
+// read as zero, so partial tiles need no special cases.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -62,9 +63,6 @@ constexpr int kStages = KD_GEMM_STAGES;             // ring of stages in LDS
 constexpr int kOpBytes = kBM * kLdsRow;             // one operand tile per stage: 16 KiB
 constexpr int kStageBytes = 2 * kOpBytes;           // A and B of one stage
 constexpr int kSmemBytes = kStages * kStageBytes;   // 128 KiB with four stages
-
-// Source of out-of-range fetches.
-__device__ __attribute__((aligned(64))) uint4 g_zero16[4];
 
 typedef f32x16_t Acc[kTM][kTN];
 
@@ -101,8 +99,23 @@ __device__ __forceinline__ int rswz(int row) {
 // 128-byte half.
 __device__ __forceinline__ int cswz(int k) { return ((k & 3) << 1) | ((k >> 1) & 1); }
 
-__device__ __forceinline__ void lds_dma16(const void* src, lds_t* dst_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(dst_wave_base), 16, 0, 0);
+// LDS-DMA through a buffer resource (buffer_load_dwordx4 ... lds): the
+// resource holds a wave-uniform base and a byte count, each lane adds a 32-bit
+// offset, and an offset at or beyond the count reads as zero without touching
+// memory. So the per-lane offsets of a tile are computed once, each stage
+// only moves the uniform base, and rows or K-tails outside the operand need
+// no per-lane pointer arithmetic or selects.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kOOB = int(0x80000000u);  // an offset beyond every record count used here
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit dwords, no swizzle
+
+__device__ __forceinline__ rsrc_t make_rsrc(const char* base, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, nbytes, kRsrcWord3);
+}
+__device__ __forceinline__ void lds_dma16(rsrc_t rs, int voff, lds_t* dst_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, reinterpret_cast<lds_void_t*>(dst_wave_base), 16,
+                                           voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ u32x4_t lds_read16(const lds_t* p) {
@@ -132,20 +145,42 @@ __device__ __forceinline__ u32x2_t lds_read_tr8(const lds_t* p) {
 struct RowDirect {
   static constexpr int kDma = kOpBytes / 1024 / 4;  // LDS-DMA instructions per wave and stage
   static constexpr int kChunks = kLdsRow / 16;       // 16-byte chunks per row
-  // 256 rows × kLdsRow = blocks of 1 KiB (1024/kLdsRow rows); each wave copies kDma blocks.
-  __device__ __forceinline__ void fetch(const RowOp& op, int r0, int kt, lds_t* tile, int wave,
-                                        int lane, int) {
-    const char* zero = reinterpret_cast<const char*>(g_zero16);
+  static constexpr int kRowsPerBlk = 1024 / kLdsRow;
+  // 256 rows × kLdsRow = blocks of 1 KiB (kRowsPerBlk rows); each wave copies
+  // kDma blocks. Stage kt of the tile starting at row r0 is read from
+  // base + r0·ld + kt·kLdsRow; lane offsets are row·ld + 16·chunk. The record
+  // count stops at the tile's last valid row, so the offsets need
+  // 256·ld < 2^31 (checked by the host).
+  int voff[kDma];
+  int rows_in;
+  __device__ __forceinline__ void init(const RowOp& op, int r0, int wave, int lane) {
+    const int left = op.rows - r0;
+    rows_in = left < 0 ? 0 : left > kBM ? kBM : left;
 #pragma unroll
     for (int j = 0; j < kDma; ++j) {
-      const int blk = wave * kDma + j;
-      const int row = blk * (1024 / kLdsRow) + lane / kChunks;
+      const int row = (wave * kDma + j) * kRowsPerBlk + lane / kChunks;
       const int c = (lane % kChunks) ^ rswz(row);  // logical chunk held at physical chunk lane%kChunks
-      const int gr = r0 + row, kb = kt * kLdsRow + c * 16;
-      const char* src = (gr < op.rows && kb < op.kbytes) ? op.base + int64_t(gr) * op.ld + kb : zero;
-      lds_dma16(src, tile + blk * 1024);
+      voff[j] = row * int(op.ld) + c * 16;
     }
   }
+  __device__ __forceinline__ rsrc_t stage(const RowOp& op, int r0, int kt) const {
+    const int kb0 = kt * kLdsRow;
+    const int n = (kb0 < op.kbytes && rows_in > 0) ? rows_in * int(op.ld) - kb0 : 0;
+    return make_rsrc(op.base + int64_t(r0) * op.ld + kb0, n);
+  }
+  // The K-tail of the last stage: chunks at or past kbytes read as zero.
+  __device__ __forceinline__ void issue(rsrc_t rs, const RowOp& op, int kt, int j, lds_t* tile,
+                                        int wave, int lane) const {
+    int vo = voff[j];
+    const int rem = op.kbytes - kt * kLdsRow;
+    if (rem < kLdsRow) {
+      const int row = (wave * kDma + j) * kRowsPerBlk + lane / kChunks;
+      const int c = (lane % kChunks) ^ rswz(row);
+      vo = c * 16 < rem ? vo : kOOB;
+    }
+    lds_dma16(rs, vo, tile + (wave * kDma + j) * 1024);
+  }
+  __device__ __forceinline__ void fetch(const RowOp&, int, int, lds_t*, int) {}
   __device__ __forceinline__ void commit(lds_t*, int) {}
   // Fragment of a 32-row block: lane l holds row rb + l%32, chunk 2s + l/32.
   __device__ static __forceinline__ u32x4_t frag(const lds_t* tile, int rb, int s, int lane) {
@@ -163,20 +198,30 @@ struct RowDirect {
 struct ColDirect {  // bf16 only
   static constexpr int kK = kLdsRow / 2;            // contraction rows per stage (32 or 64)
   static constexpr int kDma = kOpBytes / 1024 / 4;  // LDS-DMA instructions per wave and stage
-  // kK K-rows × 512 B = blocks of 2 K-rows (1 KiB); each wave copies kDma blocks.
-  __device__ __forceinline__ void fetch(const ColOp& op, int c0, int kt, lds_t* tile, int wave,
-                                        int lane, int) {
-    const char* zero = reinterpret_cast<const char*>(g_zero16);
+  // kK K-rows × 512 B = blocks of 2 K-rows (1 KiB); each wave copies kDma
+  // blocks. Stage kt of the tile starting at column c0 is read from
+  // base + kt·kK·ld + 2·c0; lane offsets are k·ld + byte, or kOOB for a
+  // column past the operand. The record count stops at the last valid K-row,
+  // so the offsets need kK·ld < 2^31 (checked by the host).
+  int voff[kDma];
+  __device__ __forceinline__ void init(const ColOp& op, int c0, int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < kDma; ++j) {
-      const int blk = wave * kDma + j;
-      const int k = blk * 2 + (lane >> 5);
+      const int k = (wave * kDma + j) * 2 + (lane >> 5);
       const int lbyte = ((lane & 31) << 4) ^ (cswz(k) << 5);  // logical byte at physical (lane&31)*16
-      const int gk = kt * kK + k, cb = c0 * 2 + lbyte;
-      const char* src = (gk < op.krows && cb < op.cbytes) ? op.base + int64_t(gk) * op.ld + cb : zero;
-      lds_dma16(src, tile + blk * 1024);
+      voff[j] = c0 * 2 + lbyte < op.cbytes ? k * int(op.ld) + lbyte : kOOB;
     }
   }
+  __device__ __forceinline__ rsrc_t stage(const ColOp& op, int c0, int kt) const {
+    const int kv = op.krows - kt * kK;
+    const int n = kv > 0 ? (kv < kK ? kv : kK) * int(op.ld) - c0 * 2 : 0;
+    return make_rsrc(op.base + int64_t(kt) * kK * op.ld + c0 * 2, n);
+  }
+  __device__ __forceinline__ void issue(rsrc_t rs, const ColOp&, int, int j, lds_t* tile,
+                                        int wave, int) const {
+    lds_dma16(rs, voff[j], tile + (wave * kDma + j) * 1024);
+  }
+  __device__ __forceinline__ void fetch(const ColOp&, int, int, lds_t*, int) {}
   __device__ __forceinline__ void commit(lds_t*, int) {}
   // Fragment of a 32-column block cb..cb+31 at contraction step s (16 K):
   // lane l gets column cb + l%32 and K = 16s + 8(l/32) + 0..7, the same
@@ -211,8 +256,10 @@ struct ColReg {  // fp32 only: kLdsRow/4 K-rows per stage, 256 columns, row layo
   static constexpr int kPer = (kK / 4) * 64 / kThreads;
   // (kK/4) K-groups × (256/4) column chunks, kPer per thread. The load is
   // consumed at once (fp32 is the small, exact path, not the fast one).
-  __device__ __forceinline__ void fetch(const ColOp& op, int c0, int kt, lds_t* tile, int, int,
-                                        int tid) {
+  __device__ __forceinline__ void init(const ColOp&, int, int, int) {}
+  __device__ __forceinline__ rsrc_t stage(const ColOp&, int, int) const { return make_rsrc(nullptr, 0); }
+  __device__ __forceinline__ void issue(rsrc_t, const ColOp&, int, int, lds_t*, int, int) const {}
+  __device__ __forceinline__ void fetch(const ColOp& op, int c0, int kt, lds_t* tile, int tid) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int u = tid + i * kThreads;
@@ -293,18 +340,51 @@ __device__ __forceinline__ void issue_read(int j, Frags& f, const lds_t* A, cons
   }
 }
 
+// The LDS-DMA of one stage, spread over the MFMA slots of a step: with T
+// loads per wave, slot j issues load j / (16/T) when j is the last slot of its
+// group, so the address-free issue sits in the shadow of the MFMAs instead of
+// stalling them in one block.
+template <class LA, class OA, class LB, class OB>
+struct StageLoads {
+  static constexpr int kT = LA::kDma + LB::kDma;
+  const LA& la;
+  const LB& lb;
+  const OA& oa;
+  const OB& ob;
+  rsrc_t ra, rb;
+  int kt;
+  lds_t* fill;
+  int wave, lane;
+  __device__ __forceinline__ void operator()(int j) const {
+    if constexpr (kT > 0) {
+      static_assert((kTM * kTN) % kT == 0, "loads spread evenly over the MFMA slots");
+      constexpr int gap = kTM * kTN / kT;
+      if (j % gap == gap - 1) {
+        const int q = j / gap;
+        if (q < LA::kDma) la.issue(ra, oa, kt, q, fill, wave, lane);
+        else lb.issue(rb, ob, kt, q - LA::kDma, fill + kOpBytes, wave, lane);
+      }
+    }
+  }
+};
+struct NoLoads {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
 // One contraction step: the 16 MFMA block products on `cur`, with the reads
-// of the fragments `nxt` for step s interleaved one per MFMA. The order is
-// pinned with scheduling barriers.
-template <bool BF16, class LA, class LB>
+// of the fragments `nxt` for step s interleaved one per MFMA, and the hook's
+// DMA issues after them. The order is pinned with scheduling barriers.
+template <bool BF16, class LA, class LB, class Hook>
 __device__ __forceinline__ void step(Acc& acc, const Frags& cur, Frags& nxt, const lds_t* A,
-                                     const lds_t* B, int wm, int wn, int s, int lane) {
+                                     const lds_t* B, int wm, int wn, int s, int lane,
+                                     const Hook& hook) {
   constexpr int kReads = kTM * LA::kReads + kTN * LB::kReads;
   static_assert(kReads <= kTM * kTN, "one read per MFMA slot");
 #pragma unroll
   for (int j = 0; j < kTM * kTN; ++j) {
     mma<BF16>(acc[j / kTN][j % kTN], cur.a[j / kTN], cur.b[j % kTN]);
     if (j < kReads) issue_read<LA, LB>(j, nxt, A, B, wm, wn, s, lane);
+    hook(j);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -365,11 +445,19 @@ __device__ __forceinline__ void gemm_tile(Acc& acc, const OA& oa, int a0, const 
 
   LA la;
   LB lb;
+  la.init(oa, a0, wave, lane);
+  lb.init(ob, b0, wave, lane);
 #pragma unroll
   for (int j = 0; j < kStages - 1; ++j) {
     lds_t* const st = smem + j * kStageBytes;
-    la.fetch(oa, a0, kt0 + j, st, wave, lane, tid);
-    lb.fetch(ob, b0, kt0 + j, st + kOpBytes, wave, lane, tid);
+    const int k = kt0 + j;
+    const rsrc_t ra = la.stage(oa, a0, k), rb = lb.stage(ob, b0, k);
+#pragma unroll
+    for (int q = 0; q < LA::kDma; ++q) la.issue(ra, oa, k, q, st, wave, lane);
+#pragma unroll
+    for (int q = 0; q < LB::kDma; ++q) lb.issue(rb, ob, k, q, st + kOpBytes, wave, lane);
+    la.fetch(oa, a0, k, st, tid);
+    lb.fetch(ob, b0, k, st + kOpBytes, tid);
     la.commit(st, tid);
     lb.commit(st + kOpBytes, tid);
   }
@@ -385,16 +473,22 @@ __device__ __forceinline__ void gemm_tile(Acc& acc, const OA& oa, int a0, const 
     const int next_slot = slot + 1 == kStages ? 0 : slot + 1;
     const int fill_slot = slot == 0 ? kStages - 1 : slot - 1;  // held stage kt - 1
     lds_t* const fill = smem + fill_slot * kStageBytes;
-    la.fetch(oa, a0, kt + kStages - 1, fill, wave, lane, tid);
-    lb.fetch(ob, b0, kt + kStages - 1, fill + kOpBytes, wave, lane, tid);
+    const int kf = kt + kStages - 1;
+    const StageLoads<LA, OA, LB, OB> loads{la, lb, oa, ob, la.stage(oa, a0, kf), lb.stage(ob, b0, kf),
+                                          kf, fill, wave, lane};
+    la.fetch(oa, a0, kf, fill, tid);
+    lb.fetch(ob, b0, kf, fill + kOpBytes, tid);
     lds_wait_frags(f0);
 #pragma unroll
     for (int st = 0; st + 1 < kSteps; ++st) {
       if (st % 2 == 0) {
-        step<BF16, LA, LB>(acc, f0, f1, cur, cur + kOpBytes, wm, wn, st + 1, lane);
+        if (st == 0)
+          step<BF16, LA, LB>(acc, f0, f1, cur, cur + kOpBytes, wm, wn, st + 1, lane, loads);
+        else
+          step<BF16, LA, LB>(acc, f0, f1, cur, cur + kOpBytes, wm, wn, st + 1, lane, NoLoads{});
         if (st + 2 < kSteps) lds_wait_frags(f1);
       } else {
-        step<BF16, LA, LB>(acc, f1, f0, cur, cur + kOpBytes, wm, wn, st + 1, lane);
+        step<BF16, LA, LB>(acc, f1, f0, cur, cur + kOpBytes, wm, wn, st + 1, lane, NoLoads{});
         lds_wait_frags(f0);
       }
     }
@@ -404,7 +498,7 @@ __device__ __forceinline__ void gemm_tile(Acc& acc, const OA& oa, int a0, const 
     lds_wait_frags(f1);
     block_barrier();  // stage kt+1 landed everywhere; nobody reads stage kt any more
     const lds_t* const nxt = smem + next_slot * kStageBytes;
-    step<BF16, LA, LB>(acc, f1, f0, nxt, nxt + kOpBytes, wm, wn, 0, lane);
+    step<BF16, LA, LB>(acc, f1, f0, nxt, nxt + kOpBytes, wm, wn, 0, lane, NoLoads{});
     slot = next_slot;
   }
   wait_vmem_le<0>();

@@ -44,6 +44,11 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
   q.kt_d = cdiv(d * es, kStageRowBytes);
   q.kt_v = cdiv(q.V_pad * es, kStageRowBytes);
   if (q.C * K > (int64_t(1) << 30) || q.nb > (int64_t(1) << 30)) return KD_ERR_UNSUPPORTED;
+  // The GEMM loaders address one 256-row tile of an operand with 32-bit
+  // offsets below 2^31: a dlogits row (V_pad elements) and an H/W row
+  // (d elements) must each stay under 8 MiB.
+  if (q.V_pad * es * kTileM >= (int64_t(1) << 31) || d * es * kTileM >= (int64_t(1) << 31))
+    return KD_ERR_UNSUPPORTED;
 
   // dH = dlogits · W has a short output (C × d) and a long contraction (V):
   // split the contraction so that enough workgroups exist to fill the chip.

@@ -82,8 +82,9 @@ const char* kd_status_str(int status);
  * Bytes of workspace kd_fused_kl_fwd (pass = KD_PASS_FWD) or kd_fused_kl_bwd
  * (pass = KD_PASS_BWD) needs for these sizes. Returns 0 if the sizes are
  * invalid (the same checks the entry points make). The backward workspace
- * holds one chunk's dlogits, chunk × V elements of `dtype` (padded to the
- * kernel tile), so it grows with the chunk, never with N × V.
+ * holds the dlogits of up to two consecutive chunks, 2 × chunk × V elements
+ * of `dtype` (padded to the kernel tile), so it grows with the chunk, never
+ * with N × V.
  */
 size_t kd_fused_kl_workspace_bytes(int pass, int64_t N, int64_t d, int64_t V, int64_t K,
                                    int64_t chunk, int dtype);
@@ -101,6 +102,10 @@ size_t kd_fused_kl_workspace_bytes(int pass, int64_t N, int64_t d, int64_t V, in
  *  loss_sum  [1] float32 — Σ_r loss_tok[r], reduced in a fixed order.
  *
  * N = 0 writes loss_sum = 0. Rows are processed `chunk` at a time.
+ *
+ * Returns KD_ERR_UNSUPPORTED for sizes the kernels do not take: K > 16383,
+ * d > 2^20, N >= 2^31, or a padded vocabulary row of 8 MiB or more
+ * (V > 4,194,048 in bf16, V > 2,096,896 in float32).
  */
 int kd_fused_kl_fwd(const void* H, const void* W, int dtype, const int32_t* topk_idx,
                     const float* topk_logp, int64_t N, int64_t d, int64_t V, int64_t K,

@@ -109,7 +109,7 @@ INV, UNS, WSE = _lib.KD_ERR_INVALID_ARG, _lib.KD_ERR_UNSUPPORTED, _lib.KD_ERR_WO
 @pytest.mark.parametrize("kw,want", [
     (dict(N=-1), INV), (dict(d=0), INV), (dict(V=0), INV), (dict(K=0), INV), (dict(K=1001), INV),
     (dict(C=0), INV), (dict(C=-5), INV), (dict(dt=2), INV), (dict(d=63), INV),
-    (dict(K=20000, V=100000), UNS), (dict(V=(1 << 28) + 1), UNS),
+    (dict(K=20000, V=100000), UNS), (dict(V=(1 << 28) + 1), UNS), (dict(V=1 << 22), UNS),
     (dict(H=None), INV), (dict(W=None), INV), (dict(idx=None), INV), (dict(logp=None), INV),
     (dict(lse=None), INV), (dict(loss_sum=None), INV),
     (dict(H=FAKE + 8), INV), (dict(W=FAKE + 4), INV), (dict(idx=FAKE + 2), INV),
@@ -145,3 +145,13 @@ def test_binding_fails_loudly_without_gpu_tensors():
     with pytest.raises(ValueError):
         ops.kl_forward(H, torch.zeros(10, 8), torch.zeros(4, 2, dtype=torch.int32),
                        torch.zeros(4, 2), chunk=2)
+
+
+def test_vocabulary_row_limit(L):
+    """The GEMM loaders take 32-bit offsets within a 256-row tile: a padded
+    vocabulary row must stay under 8 MiB in the compute dtype."""
+    ws = L.kd_fused_kl_workspace_bytes
+    for dt, vmax in ((_lib.KD_F32, 2096896), (_lib.KD_BF16, 4194048)):
+        for pass_ in (0, 1):
+            assert ws(pass_, 128, 64, vmax, 8, 32, dt) > 0
+            assert ws(pass_, 128, 64, vmax + 1, 8, 32, dt) == 0
