@@ -59,7 +59,11 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
   if (splits < 1) splits = 1;
   q.dh_splits = static_cast<int>(splits);
   const int64_t n_chunks = N > 0 ? cdiv(N, q.C) : 1;
-  q.dw_window = static_cast<int>(n_chunks < kDwWindow ? n_chunks : kDwWindow);
+  int64_t window = kDwRows / q.C;
+  if (window > kDwMaxWindow) window = kDwMaxWindow;
+  if (window > n_chunks) window = n_chunks;
+  if (window < 1) window = 1;
+  q.dw_window = static_cast<int>(window);
 
   size_t off = 0;
   auto take = [&](size_t bytes) {

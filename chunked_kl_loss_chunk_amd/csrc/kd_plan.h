@@ -20,10 +20,12 @@ constexpr int64_t kMaxK = (1 << 14) - 1;
 constexpr int kMaxDhSplits = 32;
 // Target number of dH workgroups per chunk (three waves of the 256 CUs).
 constexpr int kDhTargetTiles = 768;
-// dW is contracted over this many consecutive chunks at once: its fp32
+// dW is contracted over a window of consecutive chunks at once: its fp32
 // read-modify-write of V×d happens once per window instead of once per chunk,
-// for a backward scratch of window × chunk × V dlogits.
-constexpr int kDwWindow = 2;
+// for a backward scratch of window × chunk × V dlogits. The window covers
+// about kDwRows tokens (at most kDwMaxWindow chunks, at least one).
+constexpr int64_t kDwRows = 4096;
+constexpr int kDwMaxWindow = 4;
 
 struct Plan {
   int64_t N, d, V, K, chunk;

@@ -82,9 +82,10 @@ const char* kd_status_str(int status);
  * Bytes of workspace kd_fused_kl_fwd (pass = KD_PASS_FWD) or kd_fused_kl_bwd
  * (pass = KD_PASS_BWD) needs for these sizes. Returns 0 if the sizes are
  * invalid (the same checks the entry points make). The backward workspace
- * holds the dlogits of up to two consecutive chunks, 2 × chunk × V elements
- * of `dtype` (padded to the kernel tile), so it grows with the chunk, never
- * with N × V.
+ * holds the dlogits of a window of consecutive chunks, window × chunk × V
+ * elements of `dtype` (padded to the kernel tile), where the window is
+ * min(4, max(1, 4096 / chunk)) chunks; dW is contracted once per window. It
+ * grows with the chunk, never with N × V.
  */
 size_t kd_fused_kl_workspace_bytes(int pass, int64_t N, int64_t d, int64_t V, int64_t K,
                                    int64_t chunk, int dtype);
