@@ -99,6 +99,43 @@ __global__ void k_cast_f32_bf16(const float* __restrict__ src, __bf16* __restric
     dst[i] = __bf16(src[i]);
 }
 
+// dst[c][r] = src[r][c] for a [rows][cols] matrix of 16-bit elements (a bf16
+// chunk of H into the [d][tokens] layout the logit GEMM streams as a column
+// operand). dst rows are written for r < rows_pad, zero from `rows` on.
+// Needs cols % 8 == 0, rows_pad % 8 == 0 and 16-byte aligned rows.
+__global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict__ src,
+                                                     int64_t ld_src, int rows, int cols,
+                                                     uint16_t* __restrict__ dst, int64_t ld_dst,
+                                                     int rows_pad) {
+  __shared__ uint16_t t[64][66];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64, tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = tid + i * 256, rr = u >> 3, cc = (u & 7) * 8;
+    const int r = r0 + rr, c = c0 + cc;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < rows && c < cols) v = *reinterpret_cast<const uint4*>(src + int64_t(r) * ld_src + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      t[rr][cc + 2 * j] = uint16_t(w[j] & 0xFFFFu);
+      t[rr][cc + 2 * j + 1] = uint16_t(w[j] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = tid + i * 256, cc = u >> 3, rr = (u & 7) * 8;
+    const int c = c0 + cc, r = r0 + rr;
+    if (c < cols && r < rows_pad) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = uint32_t(t[rr + 2 * j][cc]) | (uint32_t(t[rr + 2 * j + 1][cc]) << 16);
+      *reinterpret_cast<uint4*>(dst + int64_t(c) * ld_dst + r) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 // Σ x[0..n) in a fixed order: contiguous per-thread ranges, then a tree.
 __global__ __launch_bounds__(1024) void k_sum_fixed(const float* __restrict__ x, int64_t n,
                                                     float* __restrict__ out) {
@@ -204,8 +241,9 @@ __global__ __launch_bounds__(256) void k_prep_scatter(const int* __restrict__ id
 // 64 vocabulary values; a token's (max, Σexp) over the tile needs one
 // cross-half shuffle and one exchange between the two waves sharing it.
 struct FwdArgs {
-  RowOp W;  // [V][d]
-  RowOp H;  // chunk rows of H, [rows][d]
+  RowOp W;   // [V][d]
+  RowOp H;   // chunk rows of H, [rows][d] (float32 path)
+  ColOp Ht;  // the same chunk transposed, [d][C_pad] (bf16 path)
   int kt;   // stages along d
   int tiles_t, tiles_v;
   int rows, V, K, nVt;
@@ -283,7 +321,10 @@ __global__ __launch_bounds__(kThreads) void k_fwd_logits(FwdArgs a) {
   const int t_base = tt * kBN, v_base = vt * kBM;
 
   Acc acc;
-  gemm_tile<BF16, RowDirect, RowOp, RowDirect, RowOp>(acc, a.W, v_base, a.H, t_base, 0, a.kt, smem);
+  if constexpr (BF16)
+    gemm_tile<BF16, RowDirect, RowOp, ColDirect, ColOp>(acc, a.W, v_base, a.Ht, t_base, 0, a.kt, smem);
+  else
+    gemm_tile<BF16, RowDirect, RowOp, RowDirect, RowOp>(acc, a.W, v_base, a.H, t_base, 0, a.kt, smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -417,7 +458,8 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const float2* __restrict__ 
 // --------------------------------------------------------------------------
 struct DlArgs {
   RowOp W;
-  RowOp H;
+  RowOp H;   // float32 path
+  ColOp Ht;  // bf16 path: the chunk transposed, [d][C_pad]
   int kt;
   int tiles_t, tiles_v;
   int rows, V, nVt;
@@ -441,7 +483,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs a) {
   const int t_base = tt * kBN, v_base = vt * kBM;
 
   Acc acc;
-  gemm_tile<BF16, RowDirect, RowOp, RowDirect, RowOp>(acc, a.W, v_base, a.H, t_base, 0, a.kt, smem);
+  if constexpr (BF16)
+    gemm_tile<BF16, RowDirect, RowOp, ColDirect, ColOp>(acc, a.W, v_base, a.Ht, t_base, 0, a.kt, smem);
+  else
+    gemm_tile<BF16, RowDirect, RowOp, RowDirect, RowOp>(acc, a.W, v_base, a.H, t_base, 0, a.kt, smem);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -759,6 +804,18 @@ void launch_prep(const Plan& p, const Ws& ws, const int32_t* idx, const float* l
   });
 }
 
+// The bf16 logit GEMMs stream the chunk of H as a column operand: transpose
+// it into [d][C_pad] once per chunk and pass that layout.
+ColOp chunk_transposed(const Plan& p, const Ws& ws, const char* Hc, int rows, hipStream_t st) {
+  uint16_t* ht = ws.at<uint16_t>(p.off_ht);
+  timed(KD_KERNEL_PREP, st, [&] {
+    hipLaunchKernelGGL(k_transpose16, dim3(cdiv(p.d, 64), cdiv(p.C_pad, 64)), dim3(256), 0, st,
+                       reinterpret_cast<const uint16_t*>(Hc), p.d, rows, int(p.d), ht, p.C_pad,
+                       int(p.C_pad));
+  });
+  return ColOp{reinterpret_cast<const char*>(ht), p.C_pad * 2, int(p.d), rows * 2};
+}
+
 void launch_reset(const Plan& p, const Ws& ws, hipStream_t st) {
   hipLaunchKernelGGL(k_fill_i32, dim3(cdiv(p.nb, 256)), dim3(256), 0, st, ws.at<int>(p.off_counts),
                      int64_t(p.nb), 0);
@@ -782,6 +839,8 @@ int run_fwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
       FwdArgs a;
       a.W = RowOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
       a.H = RowOp{static_cast<const char*>(H) + r0 * row_bytes, row_bytes, rows, int(row_bytes)};
+      a.Ht = BF16 ? chunk_transposed(p, ws, static_cast<const char*>(H) + r0 * row_bytes, rows, st)
+                  : ColOp{};
       a.kt = int(p.kt_d);
       a.tiles_t = int(cdiv(rows, kBN));
       a.tiles_v = int(p.nVt);
@@ -837,6 +896,7 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
     DlArgs a;
     a.W = RowOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
     a.H = RowOp{Hc, row_bytes, rows, int(row_bytes)};
+    a.Ht = BF16 ? chunk_transposed(p, ws, Hc, rows, st) : ColOp{};
     a.kt = int(p.kt_d);
     a.tiles_t = tiles_t;
     a.tiles_v = int(p.nVt);

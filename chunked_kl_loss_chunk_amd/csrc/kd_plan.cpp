@@ -76,6 +76,7 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
   q.off_offsets = take(sizeof(int32_t) * size_t(q.nb + 1));
   q.off_recs = take(8 * size_t(q.C * K));
   q.off_rowS = take(sizeof(float) * size_t(q.C_pad));
+  q.off_ht = dtype == KD_BF16 ? take(size_t(es) * size_t(d) * size_t(q.C_pad)) : 0;
   if (pass == KD_PASS_FWD) {
     q.off_zhit = take(sizeof(float) * size_t(q.C * K));
     q.off_part = take(8 * size_t(q.C_pad * q.nVt));

@@ -44,6 +44,7 @@ struct Plan {
   // byte offsets inside the workspace (all 256-byte aligned)
   size_t off_counts, off_offsets, off_recs, off_rowS, off_zhit, off_part, off_loss, off_flag;
   size_t off_dl, off_dhpart;
+  size_t off_ht;  // bf16: the chunk of H transposed, [d][C_pad]
   size_t total;
 };
 
