@@ -40,12 +40,22 @@ Readings where the pages are silent: the KL direction is KL(teacher ‖
 student); the temperature is 1; positions are flattened to N rows; the loss
 is a SUM over rows (a mean is the caller's g = 1/N); indices in a row must be
 distinct and inside [0, V); a cached log-prob of −inf contributes nothing.
+
+Per-token weights and the mean reduction. The pages mention sequence packing
+only as an ablation [P4, section 得到的 student]; packing needs per-position
+weights or masks. Reading: with weights w_r the accumulated loss is
+Σ_r w_r L_r, and the mean reduction divides it by Σ_r w_r (by N when no
+weights are given; a zero total weight gives a zero loss). The per-position
+losses L_r themselves stay unweighted. The gradient follows by the chain rule:
+G_r = g (w_r / den) (q_r rowsum(P)_r − P_r), with den = Σ_r w_r (mean) or 1
+(sum).
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = [
+    "reduction_weights",
     "to_f64",
     "teacher_grid",
     "student_log_softmax",
@@ -126,13 +136,32 @@ def kl_grad_logits(P: np.ndarray, logq: np.ndarray, grad: float = 1.0) -> np.nda
     return float(grad) * (q * P.sum(axis=1, keepdims=True) - P)
 
 
-def fused_kl_reference(H, W, idx, logp, grad: float = 1.0) -> dict:
+def reduction_weights(N: int, weight=None, reduction: str = "sum") -> np.ndarray:
+    """Per-row factor c_r of the accumulated loss Σ_r c_r L_r.
+
+    sum: c_r = w_r (1 without weights). mean: c_r = w_r / Σ_r' w_r' (1/N
+    without weights), and c = 0 when the total weight is 0.
+    """
+    if reduction not in ("sum", "mean"):
+        raise ValueError("reduction must be 'sum' or 'mean'")
+    w = np.ones(N) if weight is None else to_f64(weight).reshape(-1)
+    if w.shape[0] != N:
+        raise ValueError("weight must have one entry per row")
+    if reduction == "sum":
+        return w
+    den = w.sum()
+    return w / den if den != 0 else np.zeros(N)
+
+
+def fused_kl_reference(H, W, idx, logp, grad: float = 1.0, weight=None,
+                       reduction: str = "sum") -> dict:
     """Dense forward + backward of the top-K KL loss, all in float64.
 
     Inputs: H [N, d], W [V, d] (any float dtype; upcast exactly), idx int
-    [N, K], logp [N, K], and the upstream scalar ``grad`` = ∂objective/∂loss.
-    Returns loss_tok [N], loss (sum), lse [N], dlogits [N, V], dH [N, d],
-    dW [V, d].
+    [N, K], logp [N, K], the upstream scalar ``grad`` = ∂objective/∂loss,
+    optional per-row ``weight`` [N] and ``reduction`` ('sum' or 'mean').
+    Returns loss_tok [N] (unweighted), loss (the reduced total), lse [N],
+    dlogits [N, V], dH [N, d], dW [V, d].
     """
     H = to_f64(H)
     W = to_f64(W)
@@ -140,12 +169,13 @@ def fused_kl_reference(H, W, idx, logp, grad: float = 1.0) -> dict:
     P = teacher_grid(idx, logp, V)
     _, lse, logq = student_log_softmax(H, W)
     loss_tok = kl_rows(P, logq)
-    G = kl_grad_logits(P, logq, grad)
+    c = reduction_weights(H.shape[0], weight, reduction)
+    G = kl_grad_logits(P, logq, grad) * c[:, None]
     dH = G @ W
     dW = G.T @ H
     return {
         "loss_tok": loss_tok,
-        "loss": float(loss_tok.sum()),
+        "loss": float((c * loss_tok).sum()),
         "lse": lse,
         "dlogits": G,
         "dH": dH,

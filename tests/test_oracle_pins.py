@@ -323,3 +323,89 @@ def test_planted_renormalisation_is_caught():
         case = json.load(f)["cases"][0]
     out = _mutant("renormalise")(_arr(case["H"]), _arr(case["W"]), np.array(case["idx"]), _arr(case["logp"]))
     assert abs(out["loss_tok"][0] - _ev(case["expect"]["loss_tok"][0])) > 1e-2
+
+
+# --------------------------------------------------------------------------
+# per-token weights and the mean reduction
+# --------------------------------------------------------------------------
+def test_mask_equals_dropping_rows():
+    # A 0/1 mask must give exactly the loss and gradients of the kept rows
+    # alone: an independent evaluation on a smaller problem.
+    rng = np.random.default_rng(31)
+    H, W, idx, logp = _rand_case(rng, 12, 5, 40, 4)
+    keep = np.array([1, 0, 1, 1, 0, 0, 1, 1, 0, 1, 1, 0], dtype=bool)
+    for red in ("sum", "mean"):
+        got = oracle.fused_kl_reference(H, W, idx, logp, grad=0.7, weight=keep.astype(float), reduction=red)
+        sub = oracle.fused_kl_reference(H[keep], W, idx[keep], logp[keep], grad=0.7, reduction=red)
+        assert math.isclose(got["loss"], sub["loss"], rel_tol=1e-12)
+        np.testing.assert_allclose(got["dW"], sub["dW"], rtol=1e-10, atol=1e-14)
+        np.testing.assert_allclose(got["dH"][keep], sub["dH"], rtol=1e-10, atol=1e-14)
+        assert np.all(got["dH"][~keep] == 0.0)
+        np.testing.assert_allclose(got["loss_tok"][keep], sub["loss_tok"], rtol=1e-12)
+
+
+def test_weights_one_hot_and_linearity():
+    rng = np.random.default_rng(32)
+    H, W, idx, logp = _rand_case(rng, 6, 4, 30, 3)
+    base = oracle.fused_kl_reference(H, W, idx, logp)
+    for r in range(6):
+        e = np.zeros(6); e[r] = 1.0
+        assert math.isclose(oracle.fused_kl_reference(H, W, idx, logp, weight=e)["loss"],
+                            base["loss_tok"][r], rel_tol=1e-12)
+    w1, w2 = rng.random(6), rng.random(6)
+    a = oracle.fused_kl_reference(H, W, idx, logp, weight=w1)
+    b = oracle.fused_kl_reference(H, W, idx, logp, weight=w2)
+    c = oracle.fused_kl_reference(H, W, idx, logp, weight=2.0 * w1 - 3.0 * w2)
+    assert math.isclose(c["loss"], 2.0 * a["loss"] - 3.0 * b["loss"], rel_tol=1e-10)
+    np.testing.assert_allclose(c["dW"], 2.0 * a["dW"] - 3.0 * b["dW"], rtol=1e-9, atol=1e-13)
+
+
+def test_mean_reduction_definitions():
+    rng = np.random.default_rng(33)
+    H, W, idx, logp = _rand_case(rng, 8, 4, 25, 3)
+    base = oracle.fused_kl_reference(H, W, idx, logp)
+    m = oracle.fused_kl_reference(H, W, idx, logp, reduction="mean")
+    assert math.isclose(m["loss"], float(np.mean(base["loss_tok"])), rel_tol=1e-12)
+    np.testing.assert_allclose(m["dH"], base["dH"] / 8, rtol=1e-12)
+    w = rng.random(8)
+    mw = oracle.fused_kl_reference(H, W, idx, logp, weight=w, reduction="mean")
+    assert math.isclose(mw["loss"], float(np.dot(w, base["loss_tok"]) / w.sum()), rel_tol=1e-12)
+    # Scaling every weight by the same factor leaves the mean unchanged.
+    mw5 = oracle.fused_kl_reference(H, W, idx, logp, weight=5.0 * w, reduction="mean")
+    assert math.isclose(mw5["loss"], mw["loss"], rel_tol=1e-12)
+    np.testing.assert_allclose(mw5["dW"], mw["dW"], rtol=1e-10)
+    z = oracle.fused_kl_reference(H, W, idx, logp, weight=np.zeros(8), reduction="mean")
+    assert z["loss"] == 0.0 and np.all(z["dW"] == 0.0) and np.all(z["dH"] == 0.0)
+    with pytest.raises(ValueError):
+        oracle.fused_kl_reference(H, W, idx, logp, reduction="max")
+
+
+def _weighted(weight, reduction):
+    def fn(H, W, idx, logp, grad=1.0):
+        return oracle.fused_kl_reference(H, W, idx, logp, grad=grad, weight=weight, reduction=reduction)
+    return fn
+
+
+def test_weighted_mean_gradients_finite_differences():
+    rng = np.random.default_rng(34)
+    H, W, idx, logp = _rand_case(rng, 4, 3, 7, 2, wscale=2.0)
+    w = np.array([0.3, 0.0, 1.4, 0.8])
+    eH = [(i, j) for i in range(4) for j in range(3)]
+    eW = [(i, j) for i in range(7) for j in range(3)]
+    assert _fd_errors(_weighted(w, "mean"), H, W, idx, logp, 1.3, eH, eW) < 1e-6
+    assert _fd_errors(_weighted(w, "sum"), H, W, idx, logp, 0.6, eH, eW) < 1e-6
+
+
+def test_planted_unweighted_gradient_is_caught():
+    # A copy that weights the loss but forgets the weights in the gradient.
+    rng = np.random.default_rng(35)
+    H, W, idx, logp = _rand_case(rng, 4, 3, 7, 2, wscale=2.0)
+    w = np.array([0.3, 0.0, 1.4, 0.8])
+
+    def broken(H, W, idx, logp, grad=1.0):
+        out = oracle.fused_kl_reference(H, W, idx, logp, grad=grad)
+        out["loss"] = float(np.dot(w, out["loss_tok"]))
+        return out
+    eH = [(i, j) for i in range(4) for j in range(3)]
+    eW = [(i, j) for i in range(7) for j in range(3)]
+    assert _fd_errors(broken, H, W, idx, logp, 1.0, eH, eW) > 1e-3
