@@ -136,22 +136,46 @@ __global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict_
   }
 }
 
-// Σ x[0..n) in a fixed order: contiguous per-thread ranges, then a tree.
-__global__ __launch_bounds__(1024) void k_sum_fixed(const float* __restrict__ x, int64_t n,
-                                                    float* __restrict__ out) {
-  __shared__ float sh[1024];
+// Σ w_i x_i and Σ w_i over i < n in a fixed order (contiguous per-thread
+// ranges, then a tree); w == nullptr means every w_i = 1. One block of 1024.
+__device__ __forceinline__ float2 fixed_wsum(const float* __restrict__ x, const float* __restrict__ w,
+                                             int64_t n, float2* sh) {
   const int t = threadIdx.x;
   const int64_t per = (n + 1023) / 1024;
   const int64_t b = t * per, e = b + per < n ? b + per : n;
-  float s = 0.f;
-  for (int64_t i = b; i < e; ++i) s += x[i];
-  sh[t] = s;
+  float sx = 0.f, sw = 0.f;
+  for (int64_t i = b; i < e; ++i) {
+    const float wi = w ? w[i] : 1.f;
+    if (x) sx += wi * x[i];
+    sw += wi;
+  }
+  sh[t] = make_float2(sx, sw);
   __syncthreads();
-  for (int w = 512; w >= 1; w >>= 1) {
-    if (t < w) sh[t] += sh[t + w];
+  for (int h = 512; h >= 1; h >>= 1) {
+    if (t < h) sh[t] = make_float2(sh[t].x + sh[t + h].x, sh[t].y + sh[t + h].y);
     __syncthreads();
   }
-  if (t == 0) out[0] = sh[0];
+  return sh[0];
+}
+
+// The accumulated loss: Σ_r w_r L_r, divided by Σ_r w_r for the mean (a zero
+// total weight gives 0).
+__global__ __launch_bounds__(1024) void k_loss_reduce(const float* __restrict__ loss,
+                                                      const float* __restrict__ w, int64_t n,
+                                                      int mean, float* __restrict__ out) {
+  __shared__ float2 sh[1024];
+  const float2 s = fixed_wsum(loss, w, n, sh);
+  if (threadIdx.x == 0) out[0] = mean ? (s.y != 0.f ? s.x / s.y : 0.f) : s.x;
+}
+
+// The upstream gradient each row's dlogits is scaled by, before its weight:
+// g for the sum, g / Σ_r w_r for the mean (0 for a zero total weight).
+__global__ __launch_bounds__(1024) void k_grad_scale(const float* __restrict__ grad,
+                                                     const float* __restrict__ w, int64_t n,
+                                                     int mean, float* __restrict__ out) {
+  __shared__ float2 sh[1024];
+  const float2 s = fixed_wsum(nullptr, w, mean ? n : 0, sh);
+  if (threadIdx.x == 0) out[0] = mean ? (s.y != 0.f ? grad[0] / s.y : 0.f) : grad[0];
 }
 
 // --------------------------------------------------------------------------
@@ -467,7 +491,8 @@ struct DlArgs {
   const uint2* recs;
   const float* lse;   // chunk's lse (forward output)
   const float* rowS;  // chunk's S_r
-  const float* grad;  // device scalar g
+  const float* grad;  // device scalar: g, or g / Σw for the mean
+  const float* w;     // chunk's per-token weights, or nullptr (all 1)
   void* dl;           // [C_pad, V_pad] of the compute dtype, token-major
   int64_t ld_dl;      // elements
 };
@@ -503,7 +528,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs a) {
     const int tok = t_base + acc_col(wn, b, lane);
     const bool tok_ok = tok < a.rows;
     const float l = tok_ok ? a.lse[tok] : 0.f;
-    const float gs = tok_ok ? g * a.rowS[tok] : 0.f;
+    const float gs = tok_ok ? g * (a.w ? a.w[tok] : 1.f) * a.rowS[tok] : 0.f;
     if (full) {
 #pragma unroll
       for (int t = 0; t < kTM; ++t)
@@ -565,7 +590,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs a) {
         const float p = __uint_as_float(__builtin_amdgcn_readlane(r.y, j));
         const int tok = int(x & 255u), voc = int((x >> 8) & 1023u);
         const int wr = voc - wm * kWTM, wc = tok - wn * kWTN;
-        const float v = staged_at(region, wr, wc) - g * p;
+        const float gw = a.w ? g * a.w[t_base + tok] : g;
+        const float v = staged_at(region, wr, wc) - gw * p;
         if (lane == acc_owner(wr, wc).lane) dl[int64_t(t_base + tok) * a.ld_dl + v_base + voc] = T(v);
       }
     }
@@ -827,7 +853,8 @@ using ColLoad = typename std::conditional<BF16, ColDirect, ColReg>::type;
 
 template <bool BF16>
 int run_fwd(const Plan& p, const void* H, const void* W, const int32_t* idx, const float* logp,
-            float* loss_tok, float* lse, float* loss_sum, void* workspace, hipStream_t st) {
+            const float* weight, int mean, float* loss_tok, float* lse, float* loss_sum,
+            void* workspace, hipStream_t st) {
   Ws ws{static_cast<char*>(workspace), p};
   float* loss = loss_tok ? loss_tok : ws.at<float>(p.off_loss);
   if (p.N > 0) {
@@ -862,14 +889,14 @@ int run_fwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
       });
     }
   }
-  hipLaunchKernelGGL(k_sum_fixed, dim3(1), dim3(1024), 0, st, loss, p.N, loss_sum);
+  hipLaunchKernelGGL(k_loss_reduce, dim3(1), dim3(1024), 0, st, loss, weight, p.N, mean, loss_sum);
   return launch_status();
 }
 
 template <bool BF16>
 int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, const float* logp,
-            const float* lse, const float* grad, void* dH, float* dW, int accumulate,
-            void* workspace, hipStream_t st) {
+            const float* weight, int mean, const float* lse, const float* grad, void* dH, float* dW,
+            int accumulate, void* workspace, hipStream_t st) {
   Ws ws{static_cast<char*>(workspace), p};
   if (p.N == 0) {
     if (dW && !accumulate)
@@ -877,6 +904,8 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
     return launch_status();
   }
   launch_reset(p, ws, st);
+  float* const gscale = ws.at<float>(p.off_gscale);
+  hipLaunchKernelGGL(k_grad_scale, dim3(1), dim3(1024), 0, st, grad, weight, p.N, mean, gscale);
   const int64_t row_bytes = p.d * p.es;
   const int k_per_stage = kLdsRow / p.es;
   auto dh_kernel = k_bwd_dh<BF16, ColLoad<BF16>>;
@@ -907,7 +936,8 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
     a.recs = ws.at<uint2>(p.off_recs);
     a.lse = lse + r0;
     a.rowS = ws.at<float>(p.off_rowS);
-    a.grad = grad;
+    a.grad = gscale;
+    a.w = weight ? weight + r0 : nullptr;
     a.dl = dl_c;
     a.ld_dl = p.V_pad;
     timed(KD_KERNEL_BWD_DLOGITS, st, [&] {
@@ -995,52 +1025,76 @@ size_t kd_fused_kl_workspace_bytes(int pass, int64_t N, int64_t d, int64_t V, in
   return p.total;
 }
 
-int kd_fused_kl_fwd(const void* H, const void* W, int dtype, const int32_t* topk_idx,
-                    const float* topk_logp, int64_t N, int64_t d, int64_t V, int64_t K,
-                    int64_t chunk, float* loss_tok, float* lse, float* loss_sum, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+int kd_fused_kl_fwd_ex(const void* H, const void* W, int dtype, const int32_t* topk_idx,
+                       const float* topk_logp, const float* weight, int reduction, int64_t N,
+                       int64_t d, int64_t V, int64_t K, int64_t chunk, float* loss_tok, float* lse,
+                       float* loss, void* workspace, size_t workspace_bytes, void* stream) {
   kd::Plan p;
   const int st = kd::make_plan(KD_PASS_FWD, N, d, V, K, chunk, dtype, &p);
   if (st != KD_OK) return st;
-  if (loss_sum == nullptr || !kd::aligned(loss_sum, 4)) return KD_ERR_INVALID_ARG;
+  if (reduction != KD_REDUCE_SUM && reduction != KD_REDUCE_MEAN) return KD_ERR_INVALID_ARG;
+  if (loss == nullptr || !kd::aligned(loss, 4)) return KD_ERR_INVALID_ARG;
   if (N > 0) {
     if (!H || !W || !topk_idx || !topk_logp || !lse) return KD_ERR_INVALID_ARG;
     if (!kd::aligned(H, 16) || !kd::aligned(W, 16) || !kd::aligned(topk_idx, 4) ||
         !kd::aligned(topk_logp, 4) || !kd::aligned(lse, 4) ||
-        (loss_tok && !kd::aligned(loss_tok, 4)))
+        (loss_tok && !kd::aligned(loss_tok, 4)) || (weight && !kd::aligned(weight, 4)))
       return KD_ERR_INVALID_ARG;
   }
   if (!workspace || !kd::aligned(workspace, 256) || workspace_bytes < p.total)
     return KD_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return dtype == KD_BF16
-             ? kd::run_fwd<true>(p, H, W, topk_idx, topk_logp, loss_tok, lse, loss_sum, workspace, s)
-             : kd::run_fwd<false>(p, H, W, topk_idx, topk_logp, loss_tok, lse, loss_sum, workspace, s);
+  const float* w = N > 0 ? weight : nullptr;
+  const int mean = reduction == KD_REDUCE_MEAN;
+  return dtype == KD_BF16 ? kd::run_fwd<true>(p, H, W, topk_idx, topk_logp, w, mean, loss_tok, lse,
+                                              loss, workspace, s)
+                          : kd::run_fwd<false>(p, H, W, topk_idx, topk_logp, w, mean, loss_tok, lse,
+                                               loss, workspace, s);
 }
 
-int kd_fused_kl_bwd(const void* H, const void* W, int dtype, const int32_t* topk_idx,
-                    const float* topk_logp, const float* lse, int64_t N, int64_t d, int64_t V,
-                    int64_t K, int64_t chunk, const float* grad_loss, void* dH, float* dW,
-                    int dW_accumulate, void* workspace, size_t workspace_bytes, void* stream) {
+int kd_fused_kl_fwd(const void* H, const void* W, int dtype, const int32_t* topk_idx,
+                    const float* topk_logp, int64_t N, int64_t d, int64_t V, int64_t K,
+                    int64_t chunk, float* loss_tok, float* lse, float* loss_sum, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return kd_fused_kl_fwd_ex(H, W, dtype, topk_idx, topk_logp, nullptr, KD_REDUCE_SUM, N, d, V, K,
+                            chunk, loss_tok, lse, loss_sum, workspace, workspace_bytes, stream);
+}
+
+int kd_fused_kl_bwd_ex(const void* H, const void* W, int dtype, const int32_t* topk_idx,
+                       const float* topk_logp, const float* weight, int reduction, const float* lse,
+                       int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk,
+                       const float* grad_loss, void* dH, float* dW, int dW_accumulate,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   kd::Plan p;
   const int st = kd::make_plan(KD_PASS_BWD, N, d, V, K, chunk, dtype, &p);
   if (st != KD_OK) return st;
+  if (reduction != KD_REDUCE_SUM && reduction != KD_REDUCE_MEAN) return KD_ERR_INVALID_ARG;
   if (dW_accumulate != 0 && dW_accumulate != 1) return KD_ERR_INVALID_ARG;
   if (dW && !kd::aligned(dW, 16)) return KD_ERR_INVALID_ARG;
   if (N > 0) {
     if (!H || !W || !topk_idx || !topk_logp || !lse || !grad_loss) return KD_ERR_INVALID_ARG;
     if (!kd::aligned(H, 16) || !kd::aligned(W, 16) || !kd::aligned(topk_idx, 4) ||
         !kd::aligned(topk_logp, 4) || !kd::aligned(lse, 4) || !kd::aligned(grad_loss, 4) ||
-        (dH && !kd::aligned(dH, 16)))
+        (dH && !kd::aligned(dH, 16)) || (weight && !kd::aligned(weight, 4)))
       return KD_ERR_INVALID_ARG;
   }
   if (!workspace || !kd::aligned(workspace, 256) || workspace_bytes < p.total)
     return KD_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return dtype == KD_BF16 ? kd::run_bwd<true>(p, H, W, topk_idx, topk_logp, lse, grad_loss, dH, dW,
-                                              dW_accumulate, workspace, s)
-                          : kd::run_bwd<false>(p, H, W, topk_idx, topk_logp, lse, grad_loss, dH, dW,
-                                               dW_accumulate, workspace, s);
+  const int mean = reduction == KD_REDUCE_MEAN;
+  return dtype == KD_BF16 ? kd::run_bwd<true>(p, H, W, topk_idx, topk_logp, weight, mean, lse,
+                                              grad_loss, dH, dW, dW_accumulate, workspace, s)
+                          : kd::run_bwd<false>(p, H, W, topk_idx, topk_logp, weight, mean, lse,
+                                               grad_loss, dH, dW, dW_accumulate, workspace, s);
+}
+
+int kd_fused_kl_bwd(const void* H, const void* W, int dtype, const int32_t* topk_idx,
+                    const float* topk_logp, const float* lse, int64_t N, int64_t d, int64_t V,
+                    int64_t K, int64_t chunk, const float* grad_loss, void* dH, float* dW,
+                    int dW_accumulate, void* workspace, size_t workspace_bytes, void* stream) {
+  return kd_fused_kl_bwd_ex(H, W, dtype, topk_idx, topk_logp, nullptr, KD_REDUCE_SUM, lse, N, d, V,
+                            K, chunk, grad_loss, dH, dW, dW_accumulate, workspace, workspace_bytes,
+                            stream);
 }
 
 int kd_timing_enable(int enable) {

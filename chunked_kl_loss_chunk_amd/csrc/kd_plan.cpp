@@ -84,6 +84,7 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
     q.off_dl = q.off_dhpart = 0;
   } else {
     q.off_zhit = q.off_part = q.off_loss = 0;
+    q.off_gscale = take(256);
     // The window's chunks are packed back to back ([window·C][V_pad]); the
     // last tile of the last chunk may read (never write) up to C_pad rows.
     q.off_dl = take(size_t(es) * size_t((q.dw_window - 1) * q.C + q.C_pad) * size_t(q.V_pad));

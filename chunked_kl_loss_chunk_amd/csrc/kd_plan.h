@@ -44,7 +44,8 @@ struct Plan {
   // byte offsets inside the workspace (all 256-byte aligned)
   size_t off_counts, off_offsets, off_recs, off_rowS, off_zhit, off_part, off_loss, off_flag;
   size_t off_dl, off_dhpart;
-  size_t off_ht;  // bf16: the chunk of H transposed, [d][C_pad]
+  size_t off_ht;      // bf16: the chunk of H transposed, [d][C_pad]
+  size_t off_gscale;  // backward: the device scalar g (sum) or g / Σw (mean)
   size_t total;
 };
 

@@ -64,35 +64,65 @@ def _check_inputs(H, W, idx, logp):
     return N, d, V, idx.shape[1]
 
 
+_RED = {"sum": _lib.KD_REDUCE_SUM, "mean": _lib.KD_REDUCE_MEAN}
+
+
+def _reduction(reduction: str) -> int:
+    if reduction not in _RED:
+        raise ValueError(f"reduction must be 'sum' or 'mean', got {reduction!r}")
+    return _RED[reduction]
+
+
+def _check_weight(weight: Optional[torch.Tensor], N: int, dev: torch.device):
+    if weight is None:
+        return None
+    if (weight.shape != (N,) or weight.dtype != torch.float32 or not weight.is_contiguous()
+            or weight.device != dev):
+        raise ValueError("weight must be a contiguous fp32 [N] tensor on the inputs' device")
+    return weight
+
+
 def kl_forward(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, logp: torch.Tensor,
-               chunk: int, want_loss_tok: bool = True
+               chunk: int, want_loss_tok: bool = True, weight: Optional[torch.Tensor] = None,
+               reduction: str = "sum"
                ) -> Tuple[torch.Tensor, Optional[torch.Tensor], torch.Tensor]:
-    """Returns (loss_sum [1] fp32, loss_tok [N] fp32 or None, lse [N] fp32)."""
+    """Returns (loss [1] fp32, loss_tok [N] fp32 or None, lse [N] fp32).
+
+    ``loss`` is Σ_r w_r L_r ('sum') or that divided by Σ_r w_r ('mean'), with
+    w_r = 1 when ``weight`` is None; ``loss_tok`` holds the unweighted L_r.
+    """
     N, d, V, K = _check_inputs(H, W, idx, logp)
     dev = H.device
     dt = dtype_code(H.dtype)
+    red = _reduction(reduction)
+    weight = _check_weight(weight, N, dev)
     ws_n = workspace_bytes(_lib.KD_PASS_FWD, N, d, V, K, chunk, H.dtype)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
     loss_sum = torch.empty(1, dtype=torch.float32, device=dev)
     loss_tok = torch.empty(N, dtype=torch.float32, device=dev) if want_loss_tok else None
     lse = torch.empty(N, dtype=torch.float32, device=dev)
-    st = _lib.lib().kd_fused_kl_fwd(_p(H), _p(W), dt, _p(idx), _p(logp), N, d, V, K, chunk,
-                                     _p(loss_tok), _p(lse), _p(loss_sum), _p(ws), ws_n, _stream(dev))
-    _lib.check("kd_fused_kl_fwd", st)
+    st = _lib.lib().kd_fused_kl_fwd_ex(_p(H), _p(W), dt, _p(idx), _p(logp), _p(weight), red, N, d,
+                                        V, K, chunk, _p(loss_tok), _p(lse), _p(loss_sum), _p(ws),
+                                        ws_n, _stream(dev))
+    _lib.check("kd_fused_kl_fwd_ex", st)
     return loss_sum, loss_tok, lse
 
 
 def kl_backward(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, logp: torch.Tensor,
                 lse: torch.Tensor, grad: torch.Tensor, chunk: int, need_dH: bool = True,
                 need_dW: bool = True, dW_out: Optional[torch.Tensor] = None,
-                accumulate: bool = False) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+                accumulate: bool = False, weight: Optional[torch.Tensor] = None,
+                reduction: str = "sum") -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
     """Returns (dH [N,d] in H's dtype or None, dW [V,d] fp32 or None).
 
-    ``grad`` is a 1-element fp32 device tensor: ∂objective/∂loss_sum.
+    ``grad`` is a 1-element fp32 device tensor: ∂objective/∂loss.
     ``dW_out`` (fp32 [V,d]) is written, or added to when ``accumulate``.
+    ``weight`` and ``reduction`` must be those of the forward call.
     """
     N, d, V, K = _check_inputs(H, W, idx, logp)
     dev = H.device
+    red = _reduction(reduction)
+    weight = _check_weight(weight, N, dev)
     if lse.shape != (N,) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous fp32 [N] tensor from kl_forward")
     grad = grad.reshape(1).to(device=dev, dtype=torch.float32).contiguous()
@@ -109,10 +139,10 @@ def kl_backward(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, logp: torch
         else:
             dW = torch.empty((V, d), dtype=torch.float32, device=dev)
             accumulate = False
-    st = _lib.lib().kd_fused_kl_bwd(_p(H), _p(W), dt, _p(idx), _p(logp), _p(lse), N, d, V, K, chunk,
-                                     _p(grad), _p(dH), _p(dW), 1 if accumulate else 0, _p(ws), ws_n,
-                                     _stream(dev))
-    _lib.check("kd_fused_kl_bwd", st)
+    st = _lib.lib().kd_fused_kl_bwd_ex(_p(H), _p(W), dt, _p(idx), _p(logp), _p(weight), red,
+                                        _p(lse), N, d, V, K, chunk, _p(grad), _p(dH), _p(dW),
+                                        1 if accumulate else 0, _p(ws), ws_n, _stream(dev))
+    _lib.check("kd_fused_kl_bwd_ex", st)
     return dH, dW
 
 
@@ -127,31 +157,38 @@ def cast_f32_to_bf16(x: torch.Tensor) -> torch.Tensor:
 
 
 class FusedTopKKL(torch.autograd.Function):
-    """Σ over positions of KL(teacher top-K ‖ student softmax(H Wᵀ)).
+    """Σ over positions of w_r · KL(teacher top-K ‖ student softmax(H Wᵀ)), or
+    its weighted mean.
 
     Saves only lse [N] between the passes; the backward pass recomputes the
     logits chunk by chunk.
     """
 
     @staticmethod
-    def forward(ctx, H, W, idx, logp, chunk):
-        loss_sum, _, lse = kl_forward(H, W, idx, logp, chunk, want_loss_tok=False)
-        ctx.save_for_backward(H, W, idx, logp, lse)
+    def forward(ctx, H, W, idx, logp, chunk, weight, reduction):
+        loss, _, lse = kl_forward(H, W, idx, logp, chunk, want_loss_tok=False, weight=weight,
+                                  reduction=reduction)
+        ctx.save_for_backward(H, W, idx, logp, lse, weight)
         ctx.chunk = chunk
-        return loss_sum.reshape(())
+        ctx.reduction = reduction
+        return loss.reshape(())
 
     @staticmethod
     def backward(ctx, grad):
-        H, W, idx, logp, lse = ctx.saved_tensors
+        H, W, idx, logp, lse, weight = ctx.saved_tensors
         need_dH, need_dW = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
         dH, dW = kl_backward(H, W, idx, logp, lse, grad, ctx.chunk, need_dH=need_dH,
-                             need_dW=need_dW)
+                             need_dW=need_dW, weight=weight, reduction=ctx.reduction)
         if dW is not None and W.dtype == torch.bfloat16:
             dW = cast_f32_to_bf16(dW)
-        return dH, dW, None, None, None
+        return dH, dW, None, None, None, None, None
 
 
 def fused_kl(H: torch.Tensor, W: torch.Tensor, topk_idx: torch.Tensor, topk_logp: torch.Tensor,
-             chunk: int = 1024) -> torch.Tensor:
-    """Summed top-K KL distillation loss; differentiable in H and W."""
-    return FusedTopKKL.apply(H, W, topk_idx, topk_logp, int(chunk))
+             chunk: int = 1024, weight: Optional[torch.Tensor] = None,
+             reduction: str = "sum") -> torch.Tensor:
+    """Top-K KL distillation loss, summed (or averaged with ``reduction='mean'``)
+    over positions with optional per-position ``weight`` (fp32 [N], e.g. a
+    0/1 mask for packed sequences); differentiable in H and W."""
+    _reduction(reduction)
+    return FusedTopKKL.apply(H, W, topk_idx, topk_logp, int(chunk), weight, reduction)

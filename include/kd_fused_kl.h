@@ -75,6 +75,9 @@ typedef enum { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
 /* Which pass a workspace query is for. */
 typedef enum { KD_PASS_FWD = 0, KD_PASS_BWD = 1 } kd_pass;
 
+/* How per-position losses are accumulated (the _ex entry points). */
+typedef enum { KD_REDUCE_SUM = 0, KD_REDUCE_MEAN = 1 } kd_reduction;
+
 /* Human-readable name of a status code; never NULL. */
 const char* kd_status_str(int status);
 
@@ -131,6 +134,43 @@ int kd_fused_kl_bwd(const void* H, const void* W, int dtype, const int32_t* topk
                     const float* topk_logp, const float* lse, int64_t N, int64_t d, int64_t V,
                     int64_t K, int64_t chunk, const float* grad_loss, void* dH, float* dW,
                     int dW_accumulate, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Per-position weights or masks, and the mean reduction, for packed
+ * sequences. The Hugging Face post on cheap distillation lists sequence
+ * packing among the paper's ablations (section 得到的 student). Packing
+ * needs a weight or mask per position. Its reading here:
+ *
+ *   loss = Σ_r w_r L_r                  (reduction = KD_REDUCE_SUM)
+ *   loss = Σ_r w_r L_r / Σ_r w_r        (reduction = KD_REDUCE_MEAN; 0 if Σ w = 0)
+ *
+ * with L_r the per-position KL of kd_fused_kl_fwd and the gradient scaled per
+ * row accordingly: dlogits_r = g · w_r / den · (S_r q_r − p_r), where den is
+ * Σ_r w_r for the mean and 1 for the sum.
+ *
+ *  weight     [N] float32 device pointer, or NULL for w_r = 1 (then the
+ *             mean divides by N). Any finite values; 0 masks a position.
+ *  reduction  KD_REDUCE_SUM or KD_REDUCE_MEAN; anything else is
+ *             KD_ERR_INVALID_ARG.
+ *  loss       [1] float32 — the reduced loss (the `loss_sum` of
+ *             kd_fused_kl_fwd).
+ *  loss_tok   stays the unweighted L_r.
+ *
+ * The other arguments, the workspace and the errors are those of
+ * kd_fused_kl_fwd / kd_fused_kl_bwd, which are these calls with
+ * weight = NULL and KD_REDUCE_SUM. Pass the same weight and reduction to
+ * both passes.
+ */
+int kd_fused_kl_fwd_ex(const void* H, const void* W, int dtype, const int32_t* topk_idx,
+                       const float* topk_logp, const float* weight, int reduction, int64_t N,
+                       int64_t d, int64_t V, int64_t K, int64_t chunk, float* loss_tok, float* lse,
+                       float* loss, void* workspace, size_t workspace_bytes, void* stream);
+
+int kd_fused_kl_bwd_ex(const void* H, const void* W, int dtype, const int32_t* topk_idx,
+                       const float* topk_logp, const float* weight, int reduction, const float* lse,
+                       int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk,
+                       const float* grad_loss, void* dH, float* dW, int dW_accumulate,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Element-wise float32 -> bfloat16 (round to nearest even) of n values, for

@@ -155,3 +155,39 @@ def test_vocabulary_row_limit(L):
         for pass_ in (0, 1):
             assert ws(pass_, 128, 64, vmax, 8, 32, dt) > 0
             assert ws(pass_, 128, 64, vmax + 1, 8, 32, dt) == 0
+
+
+def _fwd_ex(L, **kw):
+    a = dict(H=FAKE, W=FAKE, dt=_lib.KD_F32, idx=FAKE, logp=FAKE, w=None, red=0, N=128, d=64, V=1000,
+             K=8, C=32, loss_tok=FAKE, lse=FAKE, loss=FAKE, ws=FAKE, ws_n=1 << 40, stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.kd_fused_kl_fwd_ex(vp(a["H"]), vp(a["W"]), a["dt"], vp(a["idx"]), vp(a["logp"]),
+                                vp(a["w"]), a["red"], a["N"], a["d"], a["V"], a["K"], a["C"],
+                                vp(a["loss_tok"]), vp(a["lse"]), vp(a["loss"]), vp(a["ws"]),
+                                a["ws_n"], a["stream"])
+
+
+def _bwd_ex(L, **kw):
+    a = dict(H=FAKE, W=FAKE, dt=_lib.KD_F32, idx=FAKE, logp=FAKE, w=None, red=0, lse=FAKE, N=128,
+             d=64, V=1000, K=8, C=32, grad=FAKE, dH=FAKE, dW=FAKE, acc=0, ws=FAKE, ws_n=1 << 40,
+             stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.kd_fused_kl_bwd_ex(vp(a["H"]), vp(a["W"]), a["dt"], vp(a["idx"]), vp(a["logp"]),
+                                vp(a["w"]), a["red"], vp(a["lse"]), a["N"], a["d"], a["V"], a["K"],
+                                a["C"], vp(a["grad"]), vp(a["dH"]), vp(a["dW"]), a["acc"],
+                                vp(a["ws"]), a["ws_n"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(red=2), INV), (dict(red=-1), INV), (dict(w=FAKE + 2), INV), (dict(d=63), INV),
+    (dict(V=1 << 22), UNS), (dict(ws=None), WSE),
+])
+def test_weighted_entry_points_reject_invalid(L, kw, want):
+    assert _fwd_ex(L, **kw) == want
+    assert _bwd_ex(L, **kw) == want
+
+
+def test_weighted_forward_requires_loss_output(L):
+    assert _fwd_ex(L, loss=None) == INV
