@@ -15,4 +15,6 @@ from .kl_oracle import (  # noqa: F401
     kl_grad_logits,
     fused_kl_reference,
     rows_reference,
+    reduction_weights,
 )
+from .teacher_oracle import teacher_logits, teacher_topk_reference  # noqa: F401
