@@ -1,6 +1,7 @@
 """Fused, chunked top-K KL distillation loss for AMD MI355X (gfx950).
 
-The loss, its forward and its backward run in the HIP kernels of the in-tree
+The loss, its forward and its backward, and the offline teacher top-K cache
+that feeds it, run in the HIP kernels of the in-tree
 library ``libkdkl.so`` (C ABI: include/kd_fused_kl.h). This package only
 marshals arguments; PyTorch provides device memory and streams.
 """
@@ -12,5 +13,6 @@ from .ops import (  # noqa: F401
     fused_kl,
     kl_backward,
     kl_forward,
+    teacher_topk,
     workspace_bytes,
 )

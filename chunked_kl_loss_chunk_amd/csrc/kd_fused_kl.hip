@@ -767,6 +767,213 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dw(DwArgs a) {
 }
 
 // --------------------------------------------------------------------------
+// offline teacher cache: top-K ids by logit and their full-softmax log-probs
+// --------------------------------------------------------------------------
+// The teacher runs once and keeps the most probable tokens of every position
+// with their log-probabilities, not renormalised. Two passes over the logit
+// GEMM per chunk, no [rows, V] grid:
+//   pass 1  k_fwd_logits with no cached ids: per-tile (max, Σexp) of each row;
+//   select  lse, and τ = the K-th largest tile maximum: at least K logits of
+//           the row are ≥ τ, so every top-K logit is ≥ τ;
+//   pass 2  the same GEMM (bitwise the same logits): every logit ≥ τ is
+//           appended to its row's candidate list;
+//   finish  an exact radix select of the K-th largest (logit, −id) key among
+//           the row's candidates, then a sort of the K winners.
+
+// Order-preserving map of a float to an unsigned key, and back.
+__device__ __forceinline__ uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float fkey_inv(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// One wave per row: lse_r from the tile partials (fixed order) and τ_r, the
+// K-th largest tile maximum (bit-by-bit search of its key), or −inf when the
+// vocabulary has fewer than K tiles. Resets the row's candidate count.
+__global__ __launch_bounds__(256) void k_tk_select(const float2* __restrict__ part, int nVt,
+                                                   int rows, int K, float* __restrict__ lse_out,
+                                                   float* __restrict__ tau_out,
+                                                   int* __restrict__ cnt) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float2* pr = part + int64_t(row) * nVt;
+  float m = kNegInf, s = 0.f;
+  for (int t = lane; t < nVt; t += 64) lse_merge(m, s, pr[t].x, pr[t].y);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
+    lse_merge(m, s, m2, s2);
+  }
+  float tau = kNegInf;
+  if (nVt >= K) {
+    uint32_t T = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      int n = 0;
+      for (int t = lane; t < nVt; t += 64) n += fkey(pr[t].x) >= c ? 1 : 0;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) n += __shfl_xor(n, off);
+      if (n >= K) T = c;
+    }
+    tau = fkey_inv(T);
+  }
+  if (lane == 0) {
+    lse_out[row] = m + __logf(s);
+    tau_out[row] = tau;
+    cnt[row] = 0;
+  }
+}
+
+struct TkArgs {
+  RowOp W;   // teacher head [V][d]
+  RowOp H;   // chunk of teacher hidden states [rows][d] (float32 path)
+  ColOp Ht;  // the same chunk transposed, [d][C_pad] (bf16 path)
+  int kt;
+  int tiles_t, tiles_v;
+  int rows, V;
+  const float* tau;  // [rows]
+  int* cnt;          // [rows] candidates so far
+  uint2* cand;       // [rows][cap]: (float bits of the logit, vocabulary id)
+  int64_t cap;       // ≥ V: a row never overflows
+};
+
+// Pass 2: the logit tile again; every logit at or above its row's τ becomes a
+// candidate. A column block with no candidate in any lane is skipped whole.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_tk_candidates(TkArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
+  lds_t* smem = (lds_t*)(smem_raw);
+  const int nblk = a.tiles_t * a.tiles_v;
+  const int logical = xcd_logical(blockIdx.x, nblk);
+  const int tt = logical % a.tiles_t, vt = logical / a.tiles_t;
+  const int t_base = tt * kBN, v_base = vt * kBM;
+
+  Acc acc;
+  if constexpr (BF16)
+    gemm_tile<BF16, RowDirect, RowOp, ColDirect, ColOp>(acc, a.W, v_base, a.Ht, t_base, 0, a.kt, smem);
+  else
+    gemm_tile<BF16, RowDirect, RowOp, RowDirect, RowOp>(acc, a.W, v_base, a.H, t_base, 0, a.kt, smem);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % kWM, wn = wave / kWM;
+  const int vlim = a.V - (v_base + wm * kWTM);
+#pragma unroll
+  for (int b = 0; b < kTN; ++b) {
+    const int tok = t_base + acc_col(wn, b, lane);
+    const float tau = tok < a.rows ? a.tau[tok] : __builtin_inff();
+    float m = kNegInf;
+#pragma unroll
+    for (int t = 0; t < kTM; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[t][b][i]);
+    if (__ballot(m >= tau) == 0) continue;
+#pragma unroll
+    for (int t = 0; t < kTM; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = t * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        const float z = acc[t][b][i];
+        if (r < vlim && z >= tau) {
+          const int slot = atomicAdd(a.cnt + tok, 1);
+          a.cand[int64_t(tok) * a.cap + slot] =
+              make_uint2(__float_as_uint(z), uint32_t(v_base + wm * kWTM + r));
+        }
+      }
+  }
+}
+
+constexpr int kTkMaxK = int(kMaxTeacherK);  // the K winners are sorted in LDS
+
+// 64-bit rank key of a candidate: larger logit first, then lower id.
+__device__ __forceinline__ uint64_t tk_key(uint2 c) {
+  return (uint64_t(fkey(__uint_as_float(c.x))) << 32) | uint64_t(0xFFFFFFFFu - c.y);
+}
+
+// One workgroup per row: the K-th largest key by an 8-bit radix select over
+// the row's candidates, the K keys at or above it gathered (keys are unique,
+// so exactly K), sorted by a bitonic network, and written out with
+// logp = z − lse.
+__global__ __launch_bounds__(256) void k_tk_finish(const uint2* __restrict__ cand, int64_t cap,
+                                                   const int* __restrict__ cnt,
+                                                   const float* __restrict__ lse, int K,
+                                                   int32_t* __restrict__ idx_out,
+                                                   float* __restrict__ logp_out) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t keys[kTkMaxK];
+  __shared__ uint64_t s_prefix;
+  __shared__ int s_krem, s_sel;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int n = cnt[row];
+  const uint2* list = cand + int64_t(row) * cap;
+  if (tid == 0) {
+    s_prefix = 0;
+    s_krem = K;
+    s_sel = 0;
+  }
+  uint64_t mask = 0;
+  for (int pass = 7; pass >= 0; --pass) {
+    hist[tid] = 0u;
+    __syncthreads();
+    const uint64_t prefix = s_prefix;
+    const int shift = 8 * pass;
+    for (int i = tid; i < n; i += 256) {
+      const uint64_t key = tk_key(list[i]);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int krem = s_krem, above = 0, bin = 255;
+      for (; bin > 0; --bin) {
+        if (above + int(hist[bin]) >= krem) break;
+        above += int(hist[bin]);
+      }
+      s_krem = krem - above;
+      s_prefix = prefix | (uint64_t(bin) << shift);
+    }
+    mask |= uint64_t(255) << shift;
+    __syncthreads();
+  }
+  const uint64_t kth = s_prefix;
+  for (int i = tid; i < n; i += 256) {
+    const uint64_t key = tk_key(list[i]);
+    if (key >= kth) {
+      const int slot = atomicAdd(&s_sel, 1);
+      if (slot < kTkMaxK) keys[slot] = key;
+    }
+  }
+  __syncthreads();
+  int P = 1;
+  while (P < K) P <<= 1;
+  for (int i = K + tid; i < P; i += 256) keys[i] = 0;
+  __syncthreads();
+  // Bitonic sort of keys[0, P), descending.
+  for (int size = 2; size <= P; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P; i += 256) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool desc = (i & size) == 0;
+          const uint64_t x = keys[i], y = keys[j];
+          if (desc ? x < y : x > y) {
+            keys[i] = y;
+            keys[j] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  const float l = lse[row];
+  for (int k = tid; k < K; k += 256) {
+    const uint64_t key = keys[k];
+    idx_out[int64_t(row) * K + k] = int32_t(0xFFFFFFFFu - uint32_t(key & 0xFFFFFFFFu));
+    logp_out[int64_t(row) * K + k] = fkey_inv(uint32_t(key >> 32)) - l;
+  }
+}
+
+// --------------------------------------------------------------------------
 // host side: chunk scheduler
 // --------------------------------------------------------------------------
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -997,6 +1204,66 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
   return launch_status();
 }
 
+template <bool BF16>
+int run_teacher(const Plan& p, const void* Ht, const void* Wt, int32_t* idx, float* logp,
+                float* lse, void* workspace, hipStream_t st) {
+  Ws ws{static_cast<char*>(workspace), p};
+  if (p.N == 0) return KD_OK;
+  hipLaunchKernelGGL(k_fill_i32, dim3(cdiv(p.nb + 1, 256)), dim3(256), 0, st,
+                     ws.at<int>(p.off_offsets), int64_t(p.nb + 1), 0);
+  const int64_t row_bytes = p.d * p.es;
+  for (int64_t r0 = 0; r0 < p.N; r0 += p.C) {
+    const int rows = int(p.N - r0 < p.C ? p.N - r0 : p.C);
+    const char* Hc = static_cast<const char*>(Ht) + r0 * row_bytes;
+    FwdArgs a;
+    a.W = RowOp{static_cast<const char*>(Wt), row_bytes, int(p.V), int(row_bytes)};
+    a.H = RowOp{Hc, row_bytes, rows, int(row_bytes)};
+    a.Ht = BF16 ? chunk_transposed(p, ws, Hc, rows, st) : ColOp{};
+    a.kt = int(p.kt_d);
+    a.tiles_t = int(cdiv(rows, kBN));
+    a.tiles_v = int(p.nVt);
+    a.rows = rows;
+    a.V = int(p.V);
+    a.K = int(p.K);
+    a.nVt = int(p.nVt);
+    a.offsets = ws.at<int>(p.off_offsets);
+    a.recs = ws.at<uint2>(p.off_recs);
+    a.zhit = nullptr;  // never written: there are no cached ids
+    a.part = ws.at<float2>(p.off_part);
+    timed(KD_KERNEL_FWD_LOGITS, st, [&] {
+      hipLaunchKernelGGL(k_fwd_logits<BF16>, dim3(a.tiles_t * a.tiles_v), dim3(kThreads), 0, st,
+                         a);
+    });
+    float* const lse_c = lse ? lse + r0 : ws.at<float>(p.off_lse);
+    timed(KD_KERNEL_OTHER, st, [&] {
+      hipLaunchKernelGGL(k_tk_select, dim3(cdiv(rows, 4)), dim3(256), 0, st, a.part, a.nVt, rows,
+                         int(p.K), lse_c, ws.at<float>(p.off_tau), ws.at<int>(p.off_cnt));
+    });
+    TkArgs t;
+    t.W = a.W;
+    t.H = a.H;
+    t.Ht = a.Ht;
+    t.kt = a.kt;
+    t.tiles_t = a.tiles_t;
+    t.tiles_v = a.tiles_v;
+    t.rows = rows;
+    t.V = int(p.V);
+    t.tau = ws.at<float>(p.off_tau);
+    t.cnt = ws.at<int>(p.off_cnt);
+    t.cand = ws.at<uint2>(p.off_cand);
+    t.cap = p.V_pad;
+    timed(KD_KERNEL_FWD_LOGITS, st, [&] {
+      hipLaunchKernelGGL(k_tk_candidates<BF16>, dim3(t.tiles_t * t.tiles_v), dim3(kThreads), 0, st,
+                         t);
+    });
+    timed(KD_KERNEL_OTHER, st, [&] {
+      hipLaunchKernelGGL(k_tk_finish, dim3(rows), dim3(256), 0, st, t.cand, t.cap, t.cnt, lse_c,
+                         int(p.K), idx + r0 * p.K, logp + r0 * p.K);
+    });
+  }
+  return launch_status();
+}
+
 inline bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
 }  // namespace
@@ -1095,6 +1362,26 @@ int kd_fused_kl_bwd(const void* H, const void* W, int dtype, const int32_t* topk
   return kd_fused_kl_bwd_ex(H, W, dtype, topk_idx, topk_logp, nullptr, KD_REDUCE_SUM, lse, N, d, V,
                             K, chunk, grad_loss, dH, dW, dW_accumulate, workspace, workspace_bytes,
                             stream);
+}
+
+int kd_teacher_topk(const void* Ht, const void* Wt, int dtype, int64_t N, int64_t d, int64_t V,
+                    int64_t K, int64_t chunk, int32_t* topk_idx, float* topk_logp, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  kd::Plan p;
+  const int st = kd::make_plan(KD_PASS_TEACHER, N, d, V, K, chunk, dtype, &p);
+  if (st != KD_OK) return st;
+  if (N > 0) {
+    if (!Ht || !Wt || !topk_idx || !topk_logp) return KD_ERR_INVALID_ARG;
+    if (!kd::aligned(Ht, 16) || !kd::aligned(Wt, 16) || !kd::aligned(topk_idx, 4) ||
+        !kd::aligned(topk_logp, 4) || (lse && !kd::aligned(lse, 4)))
+      return KD_ERR_INVALID_ARG;
+  }
+  if (!workspace || !kd::aligned(workspace, 256) || workspace_bytes < p.total)
+    return KD_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return dtype == KD_BF16
+             ? kd::run_teacher<true>(p, Ht, Wt, topk_idx, topk_logp, lse, workspace, s)
+             : kd::run_teacher<false>(p, Ht, Wt, topk_idx, topk_logp, lse, workspace, s);
 }
 
 int kd_timing_enable(int enable) {

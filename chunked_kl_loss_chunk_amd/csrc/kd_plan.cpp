@@ -14,7 +14,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, int dtype,
               Plan* p) {
   if (p == nullptr) return KD_ERR_INVALID_ARG;
-  if (pass != KD_PASS_FWD && pass != KD_PASS_BWD) return KD_ERR_INVALID_ARG;
+  if (pass != KD_PASS_FWD && pass != KD_PASS_BWD && pass != KD_PASS_TEACHER)
+    return KD_ERR_INVALID_ARG;
   if (dtype != KD_F32 && dtype != KD_BF16) return KD_ERR_INVALID_ARG;
   if (N < 0 || d <= 0 || V <= 0 || K <= 0 || chunk <= 0) return KD_ERR_INVALID_ARG;
   if (K > V) return KD_ERR_INVALID_ARG;
@@ -22,6 +23,7 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
   // 16-byte rows: every H, W and dH row starts on a 16-byte boundary.
   if ((d * es) % 16 != 0) return KD_ERR_INVALID_ARG;
   if (K > kMaxK) return KD_ERR_UNSUPPORTED;
+  if (pass == KD_PASS_TEACHER && K > kMaxTeacherK) return KD_ERR_UNSUPPORTED;
   // 32-bit limits inside the kernels (row counts, tile counts, per-chunk
   // entry counts); global byte offsets are computed in 64 bits.
   if (N > (int64_t(1) << 31) - 1 || V > (int64_t(1) << 28) || d > (int64_t(1) << 20))
@@ -77,7 +79,15 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
   q.off_recs = take(8 * size_t(q.C * K));
   q.off_rowS = take(sizeof(float) * size_t(q.C_pad));
   q.off_ht = dtype == KD_BF16 ? take(size_t(es) * size_t(d) * size_t(q.C_pad)) : 0;
-  if (pass == KD_PASS_FWD) {
+  if (pass == KD_PASS_TEACHER) {
+    // No cached ids: the bucket offsets stay zero, so the logit kernel sees
+    // empty hit lists. Candidates: up to V_pad per row, so none overflows.
+    q.off_part = take(8 * size_t(q.C_pad * q.nVt));
+    q.off_lse = take(sizeof(float) * size_t(q.C_pad));
+    q.off_tau = take(sizeof(float) * size_t(q.C_pad));
+    q.off_cnt = take(sizeof(int32_t) * size_t(q.C_pad));
+    q.off_cand = take(8 * size_t(q.C_pad) * size_t(q.V_pad));
+  } else if (pass == KD_PASS_FWD) {
     q.off_zhit = take(sizeof(float) * size_t(q.C * K));
     q.off_part = take(8 * size_t(q.C_pad * q.nVt));
     q.off_loss = take(sizeof(float) * size_t(N > 0 ? N : 1));

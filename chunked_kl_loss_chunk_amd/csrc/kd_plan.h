@@ -16,6 +16,8 @@ constexpr int kTileN = 256;  // vocabulary
 constexpr int kStageRowBytes = 64;
 // Packed hit record: token-in-tile (8 bits), vocab-in-tile (10 bits), k (14 bits).
 constexpr int64_t kMaxK = (1 << 14) - 1;
+// The teacher cache producer sorts each row's K winners in LDS.
+constexpr int64_t kMaxTeacherK = 2048;
 // Upper bound on the dH split-K factor.
 constexpr int kMaxDhSplits = 32;
 // Target number of dH workgroups per chunk (three waves of the 256 CUs).
@@ -46,10 +48,13 @@ struct Plan {
   size_t off_dl, off_dhpart;
   size_t off_ht;      // bf16: the chunk of H transposed, [d][C_pad]
   size_t off_gscale;  // backward: the device scalar g (sum) or g / Σw (mean)
+  // teacher cache producer: per-row lse, threshold, candidate count, candidates
+  size_t off_lse, off_tau, off_cnt, off_cand;
   size_t total;
 };
 
-// Fills *p for the given pass (0 forward, 1 backward). Returns a kd_status.
+// Fills *p for the given pass (0 forward, 1 backward, 2 teacher cache).
+// Returns a kd_status.
 int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, int dtype,
               Plan* p);
 

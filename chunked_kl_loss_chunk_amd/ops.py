@@ -146,6 +146,33 @@ def kl_backward(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, logp: torch
     return dH, dW
 
 
+def teacher_topk(Ht: torch.Tensor, Wt: torch.Tensor, K: int, chunk: int = 1024
+                 ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Offline teacher cache of every row: (topk_idx int32 [N,K], topk_logp
+    fp32 [N,K], lse fp32 [N]); ids by logit, largest first (ties: lower id
+    first), log-probabilities under the full softmax, not renormalised."""
+    if not (Ht.is_cuda and Wt.is_cuda):
+        raise ValueError("inputs must be on the GPU")
+    if Ht.dim() != 2 or Wt.dim() != 2 or Ht.shape[1] != Wt.shape[1]:
+        raise ValueError(f"Ht [N,d] and Wt [V,d] expected, got {tuple(Ht.shape)} {tuple(Wt.shape)}")
+    if Ht.dtype != Wt.dtype:
+        raise TypeError("Ht and Wt must share a dtype")
+    if not (Ht.is_contiguous() and Wt.is_contiguous()):
+        raise ValueError("inputs must be contiguous")
+    N, d = Ht.shape
+    V = Wt.shape[0]
+    dev = Ht.device
+    ws_n = workspace_bytes(_lib.KD_PASS_TEACHER, N, d, V, K, chunk, Ht.dtype)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    idx = torch.empty((N, K), dtype=torch.int32, device=dev)
+    logp = torch.empty((N, K), dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    st = _lib.lib().kd_teacher_topk(_p(Ht), _p(Wt), dtype_code(Ht.dtype), N, d, V, K, chunk,
+                                     _p(idx), _p(logp), _p(lse), _p(ws), ws_n, _stream(dev))
+    _lib.check("kd_teacher_topk", st)
+    return idx, logp, lse
+
+
 def cast_f32_to_bf16(x: torch.Tensor) -> torch.Tensor:
     """fp32 -> bf16 (round to nearest even) in a HIP kernel."""
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():

@@ -73,7 +73,7 @@ typedef enum {
 typedef enum { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
 
 /* Which pass a workspace query is for. */
-typedef enum { KD_PASS_FWD = 0, KD_PASS_BWD = 1 } kd_pass;
+typedef enum { KD_PASS_FWD = 0, KD_PASS_BWD = 1, KD_PASS_TEACHER = 2 } kd_pass;
 
 /* How per-position losses are accumulated (the _ex entry points). */
 typedef enum { KD_REDUCE_SUM = 0, KD_REDUCE_MEAN = 1 } kd_reduction;
@@ -171,6 +171,36 @@ int kd_fused_kl_bwd_ex(const void* H, const void* W, int dtype, const int32_t* t
                        int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk,
                        const float* grad_loss, void* dH, float* dW, int dW_accumulate,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The offline teacher cache: run the teacher's output head once and keep,
+ * for every position, the K most probable tokens with their log-probabilities
+ * under the full softmax, not renormalised. Sources:
+ *  - "Distilação de LLMs mais barata: top-K offline e KL fundida cortam VRAM
+ *    em até 15x", section "As duas mudanças";
+ *  - "Hugging Face：让知识蒸馏廉价到可大规模运行", paragraph 离线蒸馏;
+ *  - "Chunkovaná KL strata ...", section "Čo dopĺňajú podrobnejšie
+ *    experimenty".
+ * The output is the topk_idx / topk_logp input of the loss.
+ *
+ *  Ht         [N, d] of `dtype` — teacher hidden states (final layer).
+ *  Wt         [V, d] of `dtype` — teacher output head.
+ *  N, d, V, K, chunk — sizes; 1 <= K <= min(V, 2048), chunk >= 1, N >= 0.
+ *  topk_idx   [N, K] int32 out — ids by logit, largest first; equal logits
+ *             are ordered by the lower id first.
+ *  topk_logp  [N, K] float32 out — z_r,idx − lse_r.
+ *  lse        [N] float32 out, or NULL — log Σ_j exp z_rj of every row.
+ *
+ * Rows are processed `chunk` at a time with two passes of the logit GEMM and
+ * no [N, V] grid: the workspace (kd_fused_kl_workspace_bytes with
+ * KD_PASS_TEACHER) holds per-row candidate lists of up to V entries of 8
+ * bytes, so it is about chunk × V × 8 bytes. The selection is exact on the
+ * float32 logits the kernels compute. Errors as for kd_fused_kl_fwd; K > 2048
+ * is KD_ERR_UNSUPPORTED.
+ */
+int kd_teacher_topk(const void* Ht, const void* Wt, int dtype, int64_t N, int64_t d, int64_t V,
+                    int64_t K, int64_t chunk, int32_t* topk_idx, float* topk_logp, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Element-wise float32 -> bfloat16 (round to nearest even) of n values, for

@@ -59,7 +59,7 @@ def test_workspace_size_rules(L):
     assert _ws(L, f, 128, 63, 1000, 8, 32, f32) == 0  # 63*4 bytes is not a multiple of 16
     assert _ws(L, f, 128, 68, 1000, 8, 32, bf) == 0   # 68*2 bytes is not a multiple of 16
     assert _ws(L, f, 128, 64, 1000, 8, 32, 7) == 0
-    assert _ws(L, 2, 128, 64, 1000, 8, 32, f32) == 0
+    assert _ws(L, 3, 128, 64, 1000, 8, 32, f32) == 0  # passes: 0 fwd, 1 bwd, 2 teacher
     assert _ws(L, f, 128, 64, 100000, 20000, 32, f32) == 0  # K beyond the record format
     # valid
     wf = _ws(L, f, 8192, 3072, 128256, 100, 1024, bf)
@@ -191,3 +191,31 @@ def test_weighted_entry_points_reject_invalid(L, kw, want):
 
 def test_weighted_forward_requires_loss_output(L):
     assert _fwd_ex(L, loss=None) == INV
+
+
+def _tk(L, **kw):
+    a = dict(Ht=FAKE, Wt=FAKE, dt=_lib.KD_BF16, N=64, d=64, V=1000, K=8, C=32, idx=FAKE, logp=FAKE,
+             lse=None, ws=FAKE, ws_n=1 << 40, stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.kd_teacher_topk(vp(a["Ht"]), vp(a["Wt"]), a["dt"], a["N"], a["d"], a["V"], a["K"],
+                             a["C"], vp(a["idx"]), vp(a["logp"]), vp(a["lse"]), vp(a["ws"]),
+                             a["ws_n"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(K=0), INV), (dict(K=1001), INV), (dict(K=2049, V=5000), UNS), (dict(d=4), INV),
+    (dict(Ht=None), INV), (dict(idx=None), INV), (dict(logp=FAKE + 2), INV), (dict(lse=FAKE + 1), INV),
+    (dict(ws=None), WSE), (dict(ws_n=1024), WSE), (dict(C=0), INV), (dict(dt=3), INV),
+])
+def test_teacher_topk_rejects_invalid(L, kw, want):
+    assert _tk(L, **kw) == want
+
+
+def test_teacher_workspace_holds_candidate_lists(L):
+    ws = L.kd_fused_kl_workspace_bytes
+    n = ws(_lib.KD_PASS_TEACHER, 4096, 4096, 128256, 100, 1024, _lib.KD_BF16)
+    assert n >= 1024 * 128256 * 8  # up to V candidates of 8 bytes per row of a chunk
+    assert ws(_lib.KD_PASS_TEACHER, 4096, 4096, 128256, 2048, 1024, _lib.KD_BF16) > 0
+    assert ws(_lib.KD_PASS_TEACHER, 4096, 4096, 128256, 2049, 1024, _lib.KD_BF16) == 0
+    assert ws(3, 4096, 4096, 128256, 100, 1024, _lib.KD_BF16) == 0
