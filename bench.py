@@ -13,7 +13,11 @@ convention (6·N·d·V, recompute not counted), peak HBM, a roofline entry for t
 dominant kernel measured live with HIP events on the launch stream, and the
 CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload 8k-head|gpt-oss-head|sweep|small]
+    python bench.py [--steps K] [--warmup W] [--workload 8k-head|gpt-oss-head|sweep|small|teacher-cache]
+
+``--workload teacher-cache`` times the offline teacher cache step instead
+(top-K ids and log-probs through an 8B-class teacher head) and prints its own
+line.
 """
 from __future__ import annotations
 
@@ -150,12 +154,112 @@ def cpu_baseline(cfg, H, W, idx, logp, rows):
     }
 
 
+def run_teacher_cache(steps, warmup, dev, no_cpu, cpu_rows):
+    """The offline teacher cache step: top-K ids + log-probs of every position
+    through an 8B-class teacher head, kd_teacher_topk against torch's
+    materialise-then-topk path on the same inputs."""
+    import torch
+
+    import chunked_kl_loss_chunk_amd as kd
+    import workload
+
+    N, d, V, K, chunk = 8192, 4096, 128256, 100, 1024
+    L = kd.lib()
+    _log(f"generating teacher head inputs N={N} d={d} V={V}")
+    Ht_c, Wt_c = workload.teacher_head_inputs(N, d, V)
+    Ht, Wt = Ht_c.to(dev), Wt_c.to(dev)
+    torch.cuda.synchronize()
+
+    def step():
+        return kd.teacher_topk(Ht, Wt, K, chunk)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    resident = torch.cuda.memory_allocated(dev)
+    L.kd_timing_enable(1)
+    _kernel_stats(L)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        idx, logp, lse = step()
+    torch.cuda.synchronize()
+    s = (time.perf_counter() - t0) / steps
+    ks = _kernel_stats(L)
+    L.kd_timing_enable(0)
+    peak = torch.cuda.max_memory_allocated(dev)
+
+    def torch_path():
+        for r0 in range(0, N, chunk):
+            z = (Ht[r0:r0 + chunk] @ Wt.T).float()
+            v, i = torch.topk(torch.log_softmax(z, dim=1), K, dim=1)
+        return i, v
+
+    for _ in range(max(1, warmup)):
+        torch_path()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        torch_path()
+    torch.cuda.synchronize()
+    s_torch = (time.perf_counter() - t0) / steps
+
+    gemm_ms = ks["fwd_logits"]["total_ms"]
+    achieved = 4.0 * N * d * V * steps / (gemm_ms / 1e3) / 1e12 if gemm_ms > 0 else 0.0
+    out = {
+        "metric": "teacher top-K cache tokens/s",
+        "value": N / s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": s * 1e3,
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic (seeded teacher hidden states and head)",
+        "config": {"workload": "teacher-head-8k", "N": N, "d": d, "V": V, "K": K, "chunk": chunk},
+        "tflops": 4.0 * N * d * V / s / 1e12,
+        "frac_of_peak": 4.0 * N * d * V / s / 1e12 / PEAK_BF16_TFLOPS,
+        "peak_hbm_bytes": int(peak),
+        "resident_input_bytes": int(resident),
+        "kernels": {k: {"avg_ms": (v["total_ms"] / v["launches"]) if v["launches"] else 0.0,
+                        "launches_per_step": v["launches"] / steps} for k, v in ks.items()},
+        "roofline": {"kernel": "fwd_logits (both passes)", "bound": "mfma", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "torch_reference": {"ms_per_step": s_torch * 1e3, "tokens_per_s": N / s_torch,
+                            "what": "bf16 matmul per 1024 rows, fp32 log_softmax, torch.topk"},
+        "cpu_baseline": None,
+    }
+    if not no_cpu:
+        import oracle
+
+        rows = min(cpu_rows, N)
+        try:
+            from threadpoolctl import threadpool_info
+
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                           if i.get("user_api") == "blas"] or [1])
+        except Exception:
+            threads = len(os.sched_getaffinity(0))
+        _log(f"cpu oracle on {rows} rows, {threads} BLAS threads")
+        t0 = time.perf_counter()
+        oracle.teacher_topk_reference(Ht_c[:rows], Wt_c, K)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": rows / dt, "unit": "tokens/s", "cores": int(threads),
+                               "kind": "oracle",
+                               "sample": f"first {rows} of {N} rows (d={d}, V={V}, K={K}), "
+                                         f"fp64 logits, lse and sort; {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="8k-head", choices=[*WORKLOADS, "sweep"])
+    ap.add_argument("--workload", default="8k-head", choices=[*WORKLOADS, "sweep", "teacher-cache"])
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -171,6 +275,10 @@ def main():
     import workload
 
     dev = torch.device("cuda:0")
+    if args.workload == "teacher-cache":
+        run_teacher_cache(args.steps, args.warmup, dev, args.no_cpu_baseline,
+                          min(args.cpu_rows, 1024))
+        return
     if args.workload == "sweep":
         for N in workload.SWEEP_N:
             cfg = workload.config(4, N=N)

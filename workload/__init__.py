@@ -34,7 +34,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Config", "CONFIGS", "config", "make_inputs", "cache_digest"]
+__all__ = ["Config", "CONFIGS", "config", "make_inputs", "cache_digest", "teacher_head_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -136,3 +136,14 @@ def cache_digest(idx: torch.Tensor, logp: torch.Tensor) -> str:
     h.update(np.ascontiguousarray(idx.numpy()).tobytes())
     h.update(np.ascontiguousarray(logp.numpy()).tobytes())
     return h.hexdigest()
+
+
+def teacher_head_inputs(N: int = 8192, d: int = 4096, V: int = 128256, seed: int = 4000):
+    """Teacher-side inputs of the offline cache step: final hidden states
+    Ht ~ N(0, 1) [N, d] and an output head Wt ~ N(0, 4/d) [V, d] (teacher
+    logits with std ≈ 2), both rounded to bf16, on the CPU. The default shape
+    is an 8B-class teacher head (d = 4096, the Llama 3 vocabulary of 128,256)
+    over 8K positions, the pages' 8K distillation setting."""
+    Ht = _normal((N, d), 1.0, seed).to(torch.bfloat16)
+    Wt = _normal((V, d), 2.0 * d ** -0.5, seed + 1).to(torch.bfloat16)
+    return Ht.contiguous(), Wt.contiguous()
