@@ -115,8 +115,31 @@ def run_gpu(cfg, steps, warmup, dev):
     kstats = _kernel_stats(L)
     L.kd_timing_enable(0)
     peak = torch.cuda.max_memory_allocated(dev)
+    # The same step captured once into a HIP graph and replayed: no host
+    # launch gaps between the ~60 kernels of a step.
+    graph_s = None
+    try:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_s = (time.perf_counter() - g0) / steps
+        del graph
+    except RuntimeError as e:  # capture unsupported here: report the eager number only
+        _log(f"graph capture skipped: {e}")
     return {
         "sec_per_step": (t1 - t0) / steps,
+        "graph_sec_per_step": graph_s,
         "kernels": kstats,
         "peak_hbm_bytes": int(peak),
         "resident_bytes": int(resident),
@@ -332,6 +355,7 @@ def main():
         "peak_hbm_bytes": r["peak_hbm_bytes"],
         "resident_input_bytes": r["resident_bytes"],
         "kernels": kernels_out,
+        "graph_ms_per_step": None if r["graph_sec_per_step"] is None else r["graph_sec_per_step"] * 1e3,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": _traffic(dom)},
         "cache_sha256": r["cache_sha256"],

@@ -179,14 +179,21 @@ __global__ __launch_bounds__(1024) void k_grad_scale(const float* __restrict__ g
 }
 
 // --------------------------------------------------------------------------
-// prep: bucket the chunk's cached entries by (row tile, vocabulary tile)
+// prep: bucket the cached entries of a group of chunks by (chunk, row tile,
+// vocabulary tile)
 // --------------------------------------------------------------------------
+// Bucket of row `row` of the group (chunks of C rows, nMt row tiles each)
+// holding vocabulary id j.
+__device__ __forceinline__ int prep_bucket(int row, int j, int C, int nMt, int nVt) {
+  return ((row / C) * nMt + (row % C) / kTileM) * nVt + j / kTileN;
+}
+
 // One wave per row. Counts valid entries per bucket and writes S_r = Σ_k p_rk.
 // Ids outside [0, V) raise `flag` and are skipped; p = 0 entries are skipped.
 __global__ __launch_bounds__(256) void k_prep_count(const int* __restrict__ idx,
                                                     const float* __restrict__ logp, int64_t r0,
-                                                    int rows, int K, int V, int nVt,
-                                                    int* __restrict__ counts,
+                                                    int rows, int C, int nMt, int K, int V,
+                                                    int nVt, int* __restrict__ counts,
                                                     float* __restrict__ rowS,
                                                     int* __restrict__ flag) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(256) void k_prep_count(const int* __restrict__ idx,
     if (!ok) atomicOr(flag, 1);
     if (ok && p > 0.f) {
       s += p;
-      atomicAdd(&counts[(row / kTileM) * nVt + j / kTileN], 1);
+      atomicAdd(&counts[prep_bucket(row, j, C, nMt, nVt)], 1);
     }
   }
   s = wave_sum(s);
@@ -238,8 +245,8 @@ __global__ __launch_bounds__(1024) void k_prep_scan(const int* __restrict__ coun
 // record touches a distinct output element.
 __global__ __launch_bounds__(256) void k_prep_scatter(const int* __restrict__ idx,
                                                       const float* __restrict__ logp, int64_t r0,
-                                                      int rows, int K, int V, int nVt,
-                                                      int* __restrict__ counts,
+                                                      int rows, int C, int nMt, int K, int V,
+                                                      int nVt, int* __restrict__ counts,
                                                       const int* __restrict__ offsets,
                                                       uint2* __restrict__ recs) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -250,9 +257,9 @@ __global__ __launch_bounds__(256) void k_prep_scatter(const int* __restrict__ id
     const int j = ir[k];
     const float p = __expf(lr[k]);
     if (j >= 0 && j < V && p > 0.f) {
-      const int b = (row / kTileM) * nVt + j / kTileN;
+      const int b = prep_bucket(row, j, C, nMt, nVt);
       const int pos = offsets[b] + atomicSub(&counts[b], 1) - 1;
-      recs[pos] = make_uint2(pack_hit(row % kTileM, j % kTileN, k), __float_as_uint(p));
+      recs[pos] = make_uint2(pack_hit((row % C) % kTileM, j % kTileN, k), __float_as_uint(p));
     }
   }
 }
@@ -1022,20 +1029,28 @@ void timed(int cls, hipStream_t st, F&& launch) {
   if (a && b) g_timing_recs.push_back(TimingRec{cls, a, b});
 }
 
+// Buckets the cached entries of the group of chunks starting at row r0.
 void launch_prep(const Plan& p, const Ws& ws, const int32_t* idx, const float* logp, int64_t r0,
-                 int rows, hipStream_t st) {
+                 hipStream_t st) {
+  const int64_t left = p.N - r0, span = p.prep_chunks * p.C;
+  const int rows = int(left < span ? left : span);
   const int nblk = int(cdiv(rows, 4));
+  const int nbg = int(cdiv(rows, p.C) * p.nb);
   timed(KD_KERNEL_PREP, st, [&] {
-    hipLaunchKernelGGL(k_prep_count, dim3(nblk), dim3(256), 0, st, idx, logp, r0, rows, int(p.K),
-                       int(p.V), int(p.nVt), ws.at<int>(p.off_counts), ws.at<float>(p.off_rowS),
-                       ws.at<int>(p.off_flag));
+    hipLaunchKernelGGL(k_prep_count, dim3(nblk), dim3(256), 0, st, idx, logp, r0, rows, int(p.C),
+                       int(p.nMt), int(p.K), int(p.V), int(p.nVt), ws.at<int>(p.off_counts),
+                       ws.at<float>(p.off_rowS), ws.at<int>(p.off_flag));
     hipLaunchKernelGGL(k_prep_scan, dim3(1), dim3(1024), 0, st, ws.at<int>(p.off_counts),
-                       ws.at<int>(p.off_offsets), int(p.nb));
+                       ws.at<int>(p.off_offsets), nbg);
     hipLaunchKernelGGL(k_prep_scatter, dim3(nblk), dim3(256), 0, st, idx, logp, r0, rows,
-                       int(p.K), int(p.V), int(p.nVt), ws.at<int>(p.off_counts),
-                       ws.at<int>(p.off_offsets), ws.at<uint2>(p.off_recs));
+                       int(p.C), int(p.nMt), int(p.K), int(p.V), int(p.nVt),
+                       ws.at<int>(p.off_counts), ws.at<int>(p.off_offsets),
+                       ws.at<uint2>(p.off_recs));
   });
 }
+
+// Bucket offsets and S_r of the chunk in slot `slot` of the current group.
+inline int64_t prep_slot(const Plan& p, int64_t r0) { return (r0 / p.C) % p.prep_chunks; }
 
 // The bf16 logit GEMMs stream the chunk of H as a column operand: transpose
 // it into [d][C_pad] once per chunk and pass that layout.
@@ -1050,8 +1065,8 @@ ColOp chunk_transposed(const Plan& p, const Ws& ws, const char* Hc, int rows, hi
 }
 
 void launch_reset(const Plan& p, const Ws& ws, hipStream_t st) {
-  hipLaunchKernelGGL(k_fill_i32, dim3(cdiv(p.nb, 256)), dim3(256), 0, st, ws.at<int>(p.off_counts),
-                     int64_t(p.nb), 0);
+  hipLaunchKernelGGL(k_fill_i32, dim3(cdiv(p.prep_chunks * p.nb, 256)), dim3(256), 0, st,
+                     ws.at<int>(p.off_counts), int64_t(p.prep_chunks * p.nb), 0);
   hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, st, ws.at<int>(p.off_flag), int64_t(64), 0);
 }
 
@@ -1069,7 +1084,8 @@ int run_fwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
     const int64_t row_bytes = p.d * p.es;
     for (int64_t r0 = 0; r0 < p.N; r0 += p.C) {
       const int rows = int(p.N - r0 < p.C ? p.N - r0 : p.C);
-      launch_prep(p, ws, idx, logp, r0, rows, st);
+      const int64_t slot = prep_slot(p, r0);
+      if (slot == 0) launch_prep(p, ws, idx, logp, r0, st);
       FwdArgs a;
       a.W = RowOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
       a.H = RowOp{static_cast<const char*>(H) + r0 * row_bytes, row_bytes, rows, int(row_bytes)};
@@ -1082,7 +1098,7 @@ int run_fwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
       a.V = int(p.V);
       a.K = int(p.K);
       a.nVt = int(p.nVt);
-      a.offsets = ws.at<int>(p.off_offsets);
+      a.offsets = ws.at<int>(p.off_offsets) + slot * p.nb;
       a.recs = ws.at<uint2>(p.off_recs);
       a.zhit = ws.at<float>(p.off_zhit);
       a.part = ws.at<float2>(p.off_part);
@@ -1123,7 +1139,8 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
   bool dw_written = accumulate != 0;
   for (int64_t r0 = 0; r0 < p.N; r0 += p.C) {
     const int rows = int(p.N - r0 < p.C ? p.N - r0 : p.C);
-    launch_prep(p, ws, idx, logp, r0, rows, st);
+    const int64_t slot = prep_slot(p, r0);
+    if (slot == 0) launch_prep(p, ws, idx, logp, r0, st);
     const char* Hc = static_cast<const char*>(H) + r0 * row_bytes;
     const int tiles_t = int(cdiv(rows, kBN));
     if (win_chunks == 0) win_r0 = r0;
@@ -1139,10 +1156,10 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
     a.rows = rows;
     a.V = int(p.V);
     a.nVt = int(p.nVt);
-    a.offsets = ws.at<int>(p.off_offsets);
+    a.offsets = ws.at<int>(p.off_offsets) + slot * p.nb;
     a.recs = ws.at<uint2>(p.off_recs);
     a.lse = lse + r0;
-    a.rowS = ws.at<float>(p.off_rowS);
+    a.rowS = ws.at<float>(p.off_rowS) + slot * p.C;
     a.grad = gscale;
     a.w = weight ? weight + r0 : nullptr;
     a.dl = dl_c;

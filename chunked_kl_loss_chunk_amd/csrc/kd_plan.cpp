@@ -66,6 +66,11 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
   if (window > n_chunks) window = n_chunks;
   if (window < 1) window = 1;
   q.dw_window = static_cast<int>(window);
+  int64_t group = kPrepBuckets / q.nb;
+  if (group > kPrepRows / q.C) group = kPrepRows / q.C;
+  if (group > n_chunks) group = n_chunks;
+  if (group < 1) group = 1;
+  q.prep_chunks = group;
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -74,10 +79,12 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
     return o;
   };
   q.off_flag = take(256);
-  q.off_counts = take(sizeof(int32_t) * size_t(q.nb));
-  q.off_offsets = take(sizeof(int32_t) * size_t(q.nb + 1));
-  q.off_recs = take(8 * size_t(q.C * K));
-  q.off_rowS = take(sizeof(float) * size_t(q.C_pad));
+  // Prep buffers of one group of chunks: bucket counts and offsets (chunk
+  // slot major), hit records, S_r.
+  q.off_counts = take(sizeof(int32_t) * size_t(q.prep_chunks * q.nb));
+  q.off_offsets = take(sizeof(int32_t) * size_t(q.prep_chunks * q.nb + 1));
+  q.off_recs = take(8 * size_t(q.prep_chunks * q.C * K));
+  q.off_rowS = take(sizeof(float) * size_t(q.prep_chunks * q.C));
   q.off_ht = dtype == KD_BF16 ? take(size_t(es) * size_t(d) * size_t(q.C_pad)) : 0;
   if (pass == KD_PASS_TEACHER) {
     // No cached ids: the bucket offsets stay zero, so the logit kernel sees

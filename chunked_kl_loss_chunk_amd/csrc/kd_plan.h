@@ -22,6 +22,10 @@ constexpr int64_t kMaxTeacherK = 2048;
 constexpr int kMaxDhSplits = 32;
 // Target number of dH workgroups per chunk (three waves of the 256 CUs).
 constexpr int kDhTargetTiles = 768;
+// The cached ids of a group of consecutive chunks are bucketed by one prep
+// pass: at most kPrepBuckets buckets and kPrepRows rows per group.
+constexpr int64_t kPrepBuckets = int64_t(1) << 20;
+constexpr int64_t kPrepRows = 65536;
 // dW is contracted over a window of consecutive chunks at once: its fp32
 // read-modify-write of V×d happens once per window instead of once per chunk,
 // for a backward scratch of window × chunk × V dlogits. The window covers
@@ -39,6 +43,7 @@ struct Plan {
   int64_t nVt;    // vocabulary tiles
   int64_t nMt;    // row tiles per chunk
   int64_t nb;     // hit buckets per chunk = nMt * nVt
+  int64_t prep_chunks;  // chunks bucketed by one prep pass
   int64_t kt_d;   // stages along d   (d * es / kStageRowBytes, rounded up)
   int64_t kt_v;   // stages along V_pad
   int dh_splits;  // split-K factor of the dH contraction

@@ -88,7 +88,8 @@ const char* kd_status_str(int status);
  * holds the dlogits of a window of consecutive chunks, window × chunk × V
  * elements of `dtype` (padded to the kernel tile), where the window is
  * min(4, max(1, 4096 / chunk)) chunks; dW is contracted once per window. It
- * grows with the chunk, never with N × V.
+ * grows with the chunk, never with N × V. Both passes also bucket the cached
+ * entries of up to 65,536 positions at a time (about 8·K bytes per position).
  */
 size_t kd_fused_kl_workspace_bytes(int pass, int64_t N, int64_t d, int64_t V, int64_t K,
                                    int64_t chunk, int dtype);

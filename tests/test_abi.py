@@ -65,17 +65,22 @@ def test_workspace_size_rules(L):
     wf = _ws(L, f, 8192, 3072, 128256, 100, 1024, bf)
     wb = _ws(L, b, 8192, 3072, 128256, 100, 1024, bf)
     assert wf > 0 and wb > 0 and wf % 256 == 0 and wb % 256 == 0
-    # the backward holds one chunk's dlogits: at least C x V_pad bf16, and
-    # it does not grow with N once N exceeds the chunk
+    # the backward holds a window of chunks' dlogits: at least C x V_pad bf16
     V_pad = (128256 + 127) // 128 * 128
     assert wb >= 1024 * V_pad * 2
-    assert _ws(L, b, 262144, 3072, 128256, 100, 1024, bf) == wb
     assert _ws(L, b, 8192, 3072, 128256, 100, 2048, bf) > wb
-    # the forward workspace is small and linear in N (a per-token buffer)
-    w1 = _ws(L, f, 32768, 3072, 128256, 100, 2048, bf)
-    w2 = _ws(L, f, 65536, 3072, 128256, 100, 2048, bf)
-    w4 = _ws(L, f, 131072, 3072, 128256, 100, 2048, bf)
-    assert 0 < w2 - w1 <= 4 * 32768 + 256 and abs((w4 - w2) - 2 * (w2 - w1)) <= 512
+    # Past the prep group of 65,536 rows the backward workspace no longer
+    # grows with N; below it, it grows by at most the bucketed cache entries
+    # (8 bytes per entry, plus S_r) of the extra rows.
+    b64 = _ws(L, b, 65536, 3072, 128256, 100, 1024, bf)
+    assert _ws(L, b, 262144, 3072, 128256, 100, 1024, bf) == b64
+    assert _ws(L, b, 1 << 20, 3072, 128256, 100, 1024, bf) == b64
+    assert 0 < b64 - wb <= (65536 - 8192) * (8 * 100 + 4) + 64 * 1024 * 4 * 4 + 4096
+    # past the group the forward workspace grows only by its per-token loss buffer
+    w1 = _ws(L, f, 65536, 3072, 128256, 100, 2048, bf)
+    w2 = _ws(L, f, 131072, 3072, 128256, 100, 2048, bf)
+    w4 = _ws(L, f, 262144, 3072, 128256, 100, 2048, bf)
+    assert 0 < w2 - w1 <= 4 * 65536 + 256 and abs((w4 - w2) - 2 * (w2 - w1)) <= 512
     # a chunk larger than N is clamped to N
     assert _ws(L, b, 100, 64, 1000, 8, 4096, f32) == _ws(L, b, 100, 64, 1000, 8, 100, f32)
 
