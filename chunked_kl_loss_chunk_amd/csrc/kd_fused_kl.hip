@@ -552,54 +552,52 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs a) {
     }
   }
 
-  // Store: four consecutive vocabulary entries of one token per lane. Only
-  // the chunk's own rows are written (the next chunk's rows follow them).
+  // Store, one 32-token column block at a time: the block is staged in LDS in
+  // fp32 (token-major, the wave's 128 vocabulary entries contiguous), the
+  // entries at cached ids become S_r q − p there, and the block leaves as
+  // 16-byte pieces that cover each token's 128 entries in one contiguous run.
+  // Only the chunk's own rows are written (the next chunk's rows follow
+  // them); vocabulary entries past V are 0 and land in the row padding.
   T* dl = reinterpret_cast<T*>(a.dl);
+  lds_f32* region = reinterpret_cast<lds_f32*>(smem) + wave * (kStageBlockBytes / 4);
+  const int sub = lane >> 4, c8 = (lane & 15) * 8;  // store mapping: 4 tokens × 16 lanes
 #pragma unroll
   for (int b = 0; b < kTN; ++b) {
-    const int64_t tok = t_base + acc_col(wn, b, lane);
-    if (tok >= a.rows) continue;
-#pragma unroll
-    for (int t = 0; t < kTM; ++t)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        T* dst = dl + tok * a.ld_dl + v_base + acc_row(wm, t, 4 * q, lane);
-        if constexpr (BF16) {
-          const uint32_t lo = uint32_t(__builtin_bit_cast(uint16_t, __bf16(acc[t][b][4 * q + 0]))) |
-                              (uint32_t(__builtin_bit_cast(uint16_t, __bf16(acc[t][b][4 * q + 1]))) << 16);
-          const uint32_t hi = uint32_t(__builtin_bit_cast(uint16_t, __bf16(acc[t][b][4 * q + 2]))) |
-                              (uint32_t(__builtin_bit_cast(uint16_t, __bf16(acc[t][b][4 * q + 3]))) << 16);
-          *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-        } else {
-          *reinterpret_cast<float4*>(dst) = make_float4(acc[t][b][4 * q], acc[t][b][4 * q + 1],
-                                                        acc[t][b][4 * q + 2], acc[t][b][4 * q + 3]);
-        }
-      }
-  }
-  // At the cached ids of this tile the value is S_r q − p, not S_r q: the
-  // lane that owns the element stores the corrected value over the one it
-  // just wrote (same thread, same address: the later store wins).
-  lds_f32* region = reinterpret_cast<lds_f32*>(smem) + wave * (kStageBlockBytes / 4);
-  for (int base = 0; base < hits.n; base += 64) {
-    const uint2 r = hits_load(hits, base, lane);
-    const uint64_t mine = hits_mine(hits, r, base, wm, wn, lane);
-    if (mine == 0) continue;
-#pragma unroll
-    for (int b = 0; b < kTN; ++b) {
+    stage_block_column(acc, b, region, lane);
+    for (int base = 0; base < hits.n; base += 64) {
+      const uint2 r = hits_load(hits, base, lane);
+      const uint64_t mine = hits_mine(hits, r, base, wm, wn, lane);
       const int wc_lane = int(r.x & 255u) - wn * kWTN;
       uint64_t mask = mine & __ballot((wc_lane >> 5) == b);
-      if (mask == 0) continue;
-      stage_block_column(acc, b, region, lane);
       while (mask) {
         const int j = __builtin_ctzll(mask);
         mask &= mask - 1;
         const uint32_t x = __builtin_amdgcn_readlane(r.x, j);
         const float p = __uint_as_float(__builtin_amdgcn_readlane(r.y, j));
         const int tok = int(x & 255u), voc = int((x >> 8) & 1023u);
-        const int wr = voc - wm * kWTM, wc = tok - wn * kWTN;
         const float gw = a.w ? g * a.w[t_base + tok] : g;
-        const float v = staged_at(region, wr, wc) - gw * p;
-        if (lane == acc_owner(wr, wc).lane) dl[int64_t(t_base + tok) * a.ld_dl + v_base + voc] = T(v);
+        if (lane == 0) region[((tok - wn * kWTN) & 31) * kColStride + voc - wm * kWTM] -= gw * p;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tl = sub + 4 * j;
+      const int64_t tok = t_base + wn * kWTN + b * 32 + tl;
+      const lds_f32* src = region + tl * kColStride + c8;
+      const f32x4_t v0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(src);
+      const f32x4_t v1 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(src + 4);
+      if (tok >= a.rows) continue;
+      T* dst = dl + tok * a.ld_dl + v_base + wm * kWTM + c8;
+      if constexpr (BF16) {
+        const auto pk = [](float lo, float hi) {
+          return uint32_t(__builtin_bit_cast(uint16_t, __bf16(lo))) |
+                 (uint32_t(__builtin_bit_cast(uint16_t, __bf16(hi))) << 16);
+        };
+        *reinterpret_cast<uint4*>(dst) =
+            make_uint4(pk(v0[0], v0[1]), pk(v0[2], v0[3]), pk(v1[0], v1[1]), pk(v1[2], v1[3]));
+      } else {
+        *reinterpret_cast<float4*>(dst) = make_float4(v0[0], v0[1], v0[2], v0[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(v1[0], v1[1], v1[2], v1[3]);
       }
     }
   }
