@@ -714,35 +714,34 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dw(DwArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % kWM, wn = wave / kWM;
-  // Each lane owns, per block, four consecutive d of one vocabulary row: one
-  // float4 of dW. Full tiles take a branch-free path that issues a whole
-  // block column's 16 loads before the first add, so the read-modify-write
-  // costs four memory round trips per tile, not 64.
+  // Full tiles: each 32-row vocabulary block of the wave is staged in LDS
+  // (fp32, vocabulary-major), then read back so that every instruction
+  // covers two whole 512-byte runs of dW rows; a block's 16 loads of the
+  // old values are issued before the first add, so the read-modify-write
+  // costs one memory round trip per block.
   const bool full = v_base + kBN <= a.V && d_base + kBM <= a.d;
   if (full) {
+    lds_f32* region = reinterpret_cast<lds_f32*>(smem) + wave * (kStageBlockBytes / 4);
+    const int vr = lane >> 5, c4 = (lane & 31) * 4;
 #pragma unroll
     for (int b = 0; b < kTN; ++b) {
-      float* row = a.dW + int64_t(v_base + acc_col(wn, b, lane)) * a.d + d_base;
-      float4 old[kTM * 4];
+      stage_block_column(acc, b, region, lane);
+      float* rows = a.dW + int64_t(v_base + wn * kWTN + b * 32) * a.d + d_base + wm * kWTM + c4;
+      float4 old[16];
       if (a.beta) {
 #pragma unroll
-        for (int t = 0; t < kTM; ++t)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            old[t * 4 + q] = *reinterpret_cast<const float4*>(row + acc_row(wm, t, 4 * q, lane));
+        for (int j = 0; j < 16; ++j) old[j] = *reinterpret_cast<const float4*>(rows + int64_t(vr + 2 * j) * a.d);
       } else {
 #pragma unroll
-        for (int i = 0; i < kTM * 4; ++i) old[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < 16; ++j) old[j] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
-      for (int t = 0; t < kTM; ++t)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 y = old[t * 4 + q];
-          *reinterpret_cast<float4*>(row + acc_row(wm, t, 4 * q, lane)) =
-              make_float4(acc[t][b][4 * q] + y.x, acc[t][b][4 * q + 1] + y.y,
-                          acc[t][b][4 * q + 2] + y.z, acc[t][b][4 * q + 3] + y.w);
-        }
+      for (int j = 0; j < 16; ++j) {
+        const f32x4_t x = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(
+            region + (vr + 2 * j) * kColStride + c4);
+        *reinterpret_cast<float4*>(rows + int64_t(vr + 2 * j) * a.d) =
+            make_float4(x[0] + old[j].x, x[1] + old[j].y, x[2] + old[j].z, x[3] + old[j].w);
+      }
     }
     return;
   }
