@@ -636,6 +636,25 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dh(DhArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % kWM, wn = wave / kWM;
+  // Full tiles of a split write their fp32 partial through LDS-staged
+  // 32-token blocks: every store instruction covers two whole 512-byte runs.
+  if (a.splits > 1 && t_base + kBN <= a.rows && d_base + kBM <= a.d) {
+    lds_f32* region = reinterpret_cast<lds_f32*>(smem) + wave * (kStageBlockBytes / 4);
+    const int vr = lane >> 5, c4 = (lane & 31) * 4;
+    float* const part = a.part + split * a.part_stride;
+#pragma unroll
+    for (int b = 0; b < kTN; ++b) {
+      stage_block_column(acc, b, region, lane);
+      float* rows = part + int64_t(t_base + wn * kWTN + b * 32) * a.d + d_base + wm * kWTM + c4;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const f32x4_t x = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(
+            region + (vr + 2 * j) * kColStride + c4);
+        *reinterpret_cast<float4*>(rows + int64_t(vr + 2 * j) * a.d) = make_float4(x[0], x[1], x[2], x[3]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < kTN; ++b) {
     const int tok = t_base + acc_col(wn, b, lane);
