@@ -60,9 +60,14 @@ def _kernel_stats(kd_lib):
     return {c: {"total_ms": ms[i], "launches": cnt[i]} for i, c in enumerate(_lib.KERNEL_CLASSES)}
 
 
-def _traffic(kernel: str):
+TRAFFIC_WORKLOAD = "llama3.2b-head-8k"  # the workload profiles/hbm_traffic.md was taken on
+
+
+def _traffic(kernel: str, workload_name: str = TRAFFIC_WORKLOAD):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+    was taken on this workload and on the current kernel source; else None."""
+    if workload_name != TRAFFIC_WORKLOAD:
+        return None
     path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
     if not os.path.exists(path):
         return None
@@ -357,7 +362,7 @@ def main():
         "kernels": kernels_out,
         "graph_ms_per_step": None if r["graph_sec_per_step"] is None else r["graph_sec_per_step"] * 1e3,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": _traffic(dom)},
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": _traffic(dom, cfg.name)},
         "cache_sha256": r["cache_sha256"],
     }
     if not args.no_cpu_baseline:
