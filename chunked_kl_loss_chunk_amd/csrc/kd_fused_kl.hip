@@ -12,15 +12,23 @@
 // "Fused chunked KL" paragraph: project one chunk, fold it into the running
 // loss, discard it; recompute it in backward):
 //
-//  forward   prep    bucket the chunk's top-K entries by logit tile
+//  forward   prep    bucket the top-K entries of a group of chunks by logit
+//                    tile (one pass per group of up to 65,536 rows); S_r
 //            logits  z tile = H_c Wᵀ on MFMA; per tile: row max and Σexp
 //                    (online logsumexp partials) and z at the cached ids
-//            combine lse_r from the partials; L_r = Σp·logp − Σp·z + S_r·lse_r
-//  backward  prep    as above, plus S_r = Σ_k p_rk
-//            dlogits recompute the z tile; dl = g (S_r e^{z−lse_r} − p_sparse)
-//                    in registers; write the chunk's dl once (bf16 or fp32)
-//            dH      dH_c = dl · W      (split over the vocabulary)
-//            dW      dW  += dlᵀ · H_c   (fp32 read-modify-write, chunk order fixed)
+//            combine lse_r from the partials; L_r = Σp·logp − Σp·z + S_r·lse_r;
+//                    the total Σ_r w_r L_r (or its weighted mean) in fixed order
+//  backward  prep    as above
+//            dlogits recompute the z tile; dl = g w_r (S_r e^{z−lse_r} − p_sparse)
+//                    in registers, corrected at the cached ids in LDS, written
+//                    once per chunk (bf16 or fp32)
+//            dH      dH_c = dl · W      (split over the vocabulary, fixed-order sum)
+//            dW      dW  += dlᵀ · H     (once per window of chunks; fp32
+//                    read-modify-write, chunk order fixed)
+//
+// The offline teacher cache that feeds the loss (top-K ids by logit and their
+// full-softmax log-probabilities; [P1] "As duas mudanças", [P4] 离线蒸馏) is
+// produced by two passes of the same logit GEMM (kd_teacher_topk).
 //
 // The teacher distribution stays sparse and is not renormalised ([P5] "Čo
 // dopĺňajú podrobnejšie experimenty"). The gradient is the closed form of the

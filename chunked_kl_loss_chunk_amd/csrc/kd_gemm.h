@@ -7,9 +7,9 @@
 //
 // The MFMA M dimension is the vocabulary (or d) and N is tokens (or the
 // vocabulary), so each lane's four consecutive accumulator rows are four
-// consecutive elements of the row-major output: the epilogues store 8 or 16
-// bytes per lane, and per-token reductions stay inside one lane plus one
-// cross-half shuffle.
+// consecutive elements of a row-major output row: per-token reductions stay
+// inside one lane plus one cross-half shuffle, and an epilogue that writes a
+// whole output row stages 32-column blocks in LDS first.
 //
 // A workgroup of 256 threads (4 wave64s, 2×2) owns a 256×256 output tile;
 // each wave owns 128×128 as 4×4 blocks of the 32×32 MFMA (256 fp32
@@ -33,6 +33,12 @@
 // Operands are read through buffer resources whose record counts end at the
 // operand's last valid row (or K-row): out-of-range rows, columns and K-tails
 // read as zero, so partial tiles need no special cases.
+//
+// A DMA loader computes its lanes' offsets once per tile (init), gives the
+// uniform resource of a stage (stage) and issues one of its kDma loads
+// (issue); the pipeline spreads a stage's loads over the MFMA slots of a
+// step. The register loader (ColReg) has no DMA and loads and writes a stage
+// in fetch instead.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -514,20 +520,6 @@ __device__ __forceinline__ int acc_row(int wm, int a, int i, int lane) {
 }
 __device__ __forceinline__ int acc_col(int wn, int b, int lane) {
   return wn * kWTN + b * 32 + (lane & 31);
-}
-
-// Inverse for element (wr, wc) of a wave's 128×128 sub-tile: the owning lane,
-// the (uniform) block index a*kTN + b, and the register inside the block.
-struct Owner {
-  int lane, blk, reg;
-};
-__device__ __forceinline__ Owner acc_owner(int wr, int wc) {
-  const int rr = wr & 31;
-  Owner o;
-  o.lane = (wc & 31) + 32 * ((rr >> 2) & 1);
-  o.blk = (wr >> 5) * kTN + (wc >> 5);
-  o.reg = (rr & 3) + 4 * (rr >> 3);
-  return o;
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup i goes to
