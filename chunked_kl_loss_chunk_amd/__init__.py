@@ -10,6 +10,7 @@ from ._lib import KDError, lib, status_str  # noqa: F401
 from .ops import (  # noqa: F401
     FusedTopKKL,
     cast_f32_to_bf16,
+    check_inputs,
     fused_kl,
     kl_backward,
     kl_forward,

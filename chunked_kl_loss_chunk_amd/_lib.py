@@ -14,6 +14,7 @@ KD_OK, KD_ERR_INVALID_ARG, KD_ERR_UNSUPPORTED, KD_ERR_WORKSPACE, KD_ERR_HIP = ra
 KD_F32, KD_BF16 = 0, 1
 KD_PASS_FWD, KD_PASS_BWD, KD_PASS_TEACHER = 0, 1, 2
 KD_REDUCE_SUM, KD_REDUCE_MEAN = 0, 1
+KD_CHECK_ID_RANGE, KD_CHECK_DUPLICATE, KD_CHECK_LOGP = 1, 2, 4
 
 # Every function the header declares, with (restype, argtypes).
 _vp, _i64, _i, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
@@ -30,6 +31,7 @@ SIGNATURES = {
                                 _i64, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
     "kd_teacher_topk": (_i, [_vp, _vp, _i, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz,
                              _vp]),
+    "kd_fused_kl_check_inputs": (_i, [_vp, _vp, _i64, _i64, _i64, _vp, _vp]),
     "kd_cast_f32_to_bf16": (_i, [_vp, _vp, _i64, _vp]),
     "kd_timing_enable": (_i, [_i]),
     "kd_timing_read": (_i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),

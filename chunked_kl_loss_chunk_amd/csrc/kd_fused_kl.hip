@@ -1005,6 +1005,54 @@ __global__ __launch_bounds__(256) void k_tk_finish(const uint2* __restrict__ can
 }
 
 // --------------------------------------------------------------------------
+// debug check of the cache's preconditions (not on the hot path)
+// --------------------------------------------------------------------------
+constexpr int kCheckMaxK = 16384;  // power of two ≥ the largest K of the loss
+
+// One workgroup per row: ids in range and log-probs ≤ 0 (or −inf, never NaN),
+// then the row's ids sorted in LDS (bitonic, padded with INT_MAX) and
+// neighbours compared for duplicates. Violations are OR-ed into *flags.
+__global__ __launch_bounds__(256) void k_check_inputs(const int* __restrict__ idx,
+                                                      const float* __restrict__ logp, int K,
+                                                      int V, int* __restrict__ flags) {
+  __shared__ int ids[kCheckMaxK];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  int P = 1;
+  while (P < K) P <<= 1;
+  int bad = 0;
+  for (int k = tid; k < P; k += 256) {
+    int j = 0x7FFFFFFF;
+    if (k < K) {
+      j = idx[row * K + k];
+      const float lp = logp[row * K + k];
+      if (j < 0 || j >= V) bad |= KD_CHECK_ID_RANGE;
+      if (!(lp <= 0.f)) bad |= KD_CHECK_LOGP;  // positive, +inf or NaN
+    }
+    ids[k] = j;
+  }
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P; i += 256) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool up = (i & size) == 0;
+          const int x = ids[i], y = ids[j];
+          if (up ? x > y : x < y) {
+            ids[i] = y;
+            ids[j] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int k = tid + 1; k < K; k += 256)
+    if (ids[k] == ids[k - 1]) bad |= KD_CHECK_DUPLICATE;
+  if (bad) atomicOr(flags, bad);
+}
+
+// --------------------------------------------------------------------------
 // host side: chunk scheduler
 // --------------------------------------------------------------------------
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1423,6 +1471,23 @@ int kd_teacher_topk(const void* Ht, const void* Wt, int dtype, int64_t N, int64_
   return dtype == KD_BF16
              ? kd::run_teacher<true>(p, Ht, Wt, topk_idx, topk_logp, lse, workspace, s)
              : kd::run_teacher<false>(p, Ht, Wt, topk_idx, topk_logp, lse, workspace, s);
+}
+
+int kd_fused_kl_check_inputs(const int32_t* topk_idx, const float* topk_logp, int64_t N,
+                             int64_t K, int64_t V, int32_t* flags, void* stream) {
+  if (N < 0 || K <= 0 || V <= 0 || K > V || K > kd::kMaxK || V > (int64_t(1) << 31) - 1)
+    return KD_ERR_INVALID_ARG;
+  if (N > (int64_t(1) << 31) - 1) return KD_ERR_UNSUPPORTED;
+  if (!flags || !kd::aligned(flags, 4)) return KD_ERR_INVALID_ARG;
+  if (N > 0 && (!topk_idx || !topk_logp || !kd::aligned(topk_idx, 4) || !kd::aligned(topk_logp, 4)))
+    return KD_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(kd::k_fill_i32, dim3(1), dim3(64), 0, s, reinterpret_cast<int*>(flags),
+                     int64_t(1), 0);
+  if (N > 0)
+    hipLaunchKernelGGL(kd::k_check_inputs, dim3(unsigned(N)), dim3(256), 0, s, topk_idx, topk_logp,
+                       int(K), int(V), reinterpret_cast<int*>(flags));
+  return kd::launch_status();
 }
 
 int kd_timing_enable(int enable) {

@@ -173,6 +173,30 @@ def teacher_topk(Ht: torch.Tensor, Wt: torch.Tensor, K: int, chunk: int = 1024
     return idx, logp, lse
 
 
+def check_inputs(topk_idx: torch.Tensor, topk_logp: torch.Tensor, V: int) -> list:
+    """Debug check of the cache's preconditions on the GPU (ids in [0, V) and
+    distinct per row, log-probs <= 0 or -inf). Returns the names of the
+    violated ones (empty if all hold); synchronises the stream to read them."""
+    if not (topk_idx.is_cuda and topk_logp.is_cuda):
+        raise ValueError("inputs must be on the GPU")
+    if topk_idx.dim() != 2 or topk_idx.shape != topk_logp.shape:
+        raise ValueError("topk_idx and topk_logp must both be [N, K]")
+    if topk_idx.dtype != torch.int32 or topk_logp.dtype != torch.float32:
+        raise TypeError("topk_idx must be int32 and topk_logp float32")
+    if not (topk_idx.is_contiguous() and topk_logp.is_contiguous()):
+        raise ValueError("inputs must be contiguous")
+    N, K = topk_idx.shape
+    dev = topk_idx.device
+    flags = torch.empty(1, dtype=torch.int32, device=dev)
+    st = _lib.lib().kd_fused_kl_check_inputs(_p(topk_idx), _p(topk_logp), N, K, int(V),
+                                              _p(flags), _stream(dev))
+    _lib.check("kd_fused_kl_check_inputs", st)
+    f = int(flags.item())
+    names = [(_lib.KD_CHECK_ID_RANGE, "id out of range"), (_lib.KD_CHECK_DUPLICATE, "duplicate id"),
+             (_lib.KD_CHECK_LOGP, "log-prob > 0 or NaN")]
+    return [n for bit, n in names if f & bit]
+
+
 def cast_f32_to_bf16(x: torch.Tensor) -> torch.Tensor:
     """fp32 -> bf16 (round to nearest even) in a HIP kernel."""
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():

@@ -204,6 +204,25 @@ int kd_teacher_topk(const void* Ht, const void* Wt, int dtype, int64_t N, int64_
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Debug check of the cache preconditions the loss does not check on its hot
+ * path (not needed for correct inputs, and not called by the loss):
+ * every id in [0, V), the ids of a row distinct, every log-probability ≤ 0
+ * or −inf (never positive, +inf or NaN). The cache holds log-probabilities
+ * of the teacher's full softmax, kept without renormalisation ("Chunkovaná KL
+ * strata ...", section "Čo dopĺňajú podrobnejšie experimenty").
+ *
+ *  topk_idx  [N, K] int32, topk_logp [N, K] float32 — device pointers.
+ *  flags     [1] int32, DEVICE pointer — overwritten with the OR of
+ *            KD_CHECK_* bits of every violation found (0: all hold). Read it
+ *            after the stream reaches this call; nothing here synchronises.
+ *
+ * 1 <= K <= min(V, 16383), N >= 0; otherwise KD_ERR_INVALID_ARG.
+ */
+enum { KD_CHECK_ID_RANGE = 1, KD_CHECK_DUPLICATE = 2, KD_CHECK_LOGP = 4 };
+int kd_fused_kl_check_inputs(const int32_t* topk_idx, const float* topk_logp, int64_t N,
+                             int64_t K, int64_t V, int32_t* flags, void* stream);
+
+/*
  * Element-wise float32 -> bfloat16 (round to nearest even) of n values, for
  * callers that keep W in bf16 and want dW in W's dtype. Device pointers;
  * src and dst must not overlap.

@@ -224,3 +224,15 @@ def test_teacher_workspace_holds_candidate_lists(L):
     assert ws(_lib.KD_PASS_TEACHER, 4096, 4096, 128256, 2048, 1024, _lib.KD_BF16) > 0
     assert ws(_lib.KD_PASS_TEACHER, 4096, 4096, 128256, 2049, 1024, _lib.KD_BF16) == 0
     assert ws(3, 4096, 4096, 128256, 100, 1024, _lib.KD_BF16) == 0
+
+
+@pytest.mark.parametrize("args,want", [
+    ((FAKE, FAKE, -1, 8, 100, FAKE), INV), ((FAKE, FAKE, 10, 0, 100, FAKE), INV),
+    ((FAKE, FAKE, 10, 101, 100, FAKE), INV), ((FAKE, FAKE, 10, 16384, 20000, FAKE), INV),
+    ((FAKE, FAKE, 10, 8, 100, None), INV), ((FAKE, FAKE, 10, 8, 100, FAKE + 2), INV),
+    ((None, FAKE, 10, 8, 100, FAKE), INV), ((FAKE, FAKE + 1, 10, 8, 100, FAKE), INV),
+])
+def test_check_inputs_rejects_invalid(L, args, want):
+    vp = ctypes.c_void_p
+    idx, logp, N, K, V, flags = args
+    assert L.kd_fused_kl_check_inputs(vp(idx), vp(logp), N, K, V, vp(flags), None) == want

@@ -100,3 +100,26 @@ def test_bad_weight_and_reduction_rejected(kd):
         kd.kl_forward(Hd, Wd, id_, lp, 8, reduction="max")
     with pytest.raises(ValueError):
         kd.kl_forward(Hd, Wd, id_, lp, 8, weight=torch.ones(15, device=Hd.device))
+
+
+def test_check_inputs_flags_each_violation(kd):
+    from test_gpu_parity import _case
+    H, W, idx, logp = _case(64, 32, 500, 12, "f32", seed=47)
+    dev = torch.device("cuda:0")
+    assert kd.check_inputs(idx.to(dev), logp.to(dev), 500) == []
+    bad = idx.clone(); bad[3, 5] = 500
+    assert kd.check_inputs(bad.to(dev), logp.to(dev), 500) == ["id out of range"]
+    bad = idx.clone(); bad[10, 7] = bad[10, 2]
+    assert kd.check_inputs(bad.to(dev), logp.to(dev), 500) == ["duplicate id"]
+    badl = logp.clone(); badl[20, 0] = float("nan")
+    assert kd.check_inputs(idx.to(dev), badl.to(dev), 500) == ["log-prob > 0 or NaN"]
+    badl = logp.clone(); badl[0, 0] = 0.25; badl[1, 1] = float("-inf")  # -inf is allowed
+    assert kd.check_inputs(idx.to(dev), badl.to(dev), 500) == ["log-prob > 0 or NaN"]
+    badl = logp.clone(); badl[1, 1] = float("-inf")
+    assert kd.check_inputs(idx.to(dev), badl.to(dev), 500) == []
+    # the largest K the loss takes: one row with every id distinct, one with a repeat
+    big = torch.stack([torch.randperm(20000)[:16383], torch.randperm(20000)[:16383]]).to(torch.int32)
+    big[1, 16000] = big[1, 3]
+    lp = torch.full(big.shape, -10.0)
+    assert kd.check_inputs(big[:1].contiguous().to(dev), lp[:1].contiguous().to(dev), 20000) == []
+    assert kd.check_inputs(big.contiguous().to(dev), lp.contiguous().to(dev), 20000) == ["duplicate id"]
