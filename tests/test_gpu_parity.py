@@ -258,3 +258,48 @@ def test_full_size_sampled_dw_rows(head8k):
         ref += part["dlogits"][:, J].T @ H64[rows]
         del part
     assert max_norm_err(got["dW"][J], ref) < 2e-2
+
+
+# --------------------------------------------------------------------------
+# full size at the other configurations: the gpt-oss head (d = 2880 leaves a
+# ragged d tile; V = 201,088) and the longest point of the long-context sweep
+# (N = 262,144 in 2,048-row chunks: four prep groups, 32 dW windows). The
+# oracle checks sampled rows; dW is checked through identities that hold at
+# any size, computed on the GPU in float64.
+# --------------------------------------------------------------------------
+def _full_size_check(kd, cfg, rows_extra):
+    H, W, idx, logp = workload.make_inputs(cfg, teacher_device="cuda")
+    Hd, Wd, id_, lp = _to_dev(H, W, idx, logp)
+    loss_sum, loss_tok, lse = kd.kl_forward(Hd, Wd, id_, lp, cfg.chunk)
+    g = torch.ones(1, dtype=torch.float32, device=Hd.device)
+    dH, dW = kd.kl_backward(Hd, Wd, id_, lp, lse, g, cfg.chunk)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(cfg.N + cfg.V)
+    rows = sorted(set(rows_extra) | set(rng.integers(0, cfg.N, 8).tolist()))
+    ref = oracle.rows_reference(H, oracle.to_f64(W), idx, logp, rows)
+    sel = torch.tensor(rows, device=Hd.device)
+    assert rel_err(loss_tok[sel].double().cpu().numpy(), ref["loss_tok"]) < 2e-3
+    assert rel_err(lse[sel].double().cpu().numpy(), ref["lse"]) < 2e-3
+    assert max_norm_err(dH[sel].double().cpu().numpy(), ref["dH"]) < 2e-2
+    tot = loss_tok.double().sum().item()
+    assert abs(loss_sum.item() - tot) <= 1e-5 * abs(tot)
+    dW64 = dW.double()
+    colsum = dW64.sum(dim=0).abs().max().item()
+    assert colsum < 1e-3 * dW64.abs().max().item() * np.sqrt(cfg.V)
+    a = (dW64 * Wd.double()).sum().item()
+    b = (dH.double() * Hd.double()).sum().item()
+    assert abs(a - b) < 2e-2 * max(abs(a), abs(b), 1e-12)
+
+
+@pytest.mark.timeout(900)
+def test_full_size_gpt_oss_head(kd):
+    cfg = workload.config(5)
+    _full_size_check(kd, cfg, [0, 2047, 2048, 16383, cfg.N - 1])
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_full_size_longest_context(kd):
+    cfg = workload.config(4, N=workload.SWEEP_N[-1])
+    _full_size_check(kd, cfg, [0, 2047, 2048, 65535, 65536, 131071, 196608, cfg.N - 1])
+    torch.cuda.empty_cache()
