@@ -263,7 +263,7 @@ def test_full_size_sampled_dw_rows(head8k):
 # --------------------------------------------------------------------------
 # full size at the other configurations: the gpt-oss head (d = 2880 leaves a
 # ragged d tile; V = 201,088) and the longest point of the long-context sweep
-# (N = 262,144 in 2,048-row chunks: four prep groups, 32 dW windows). The
+# (N = 262,144 in 2,048-row chunks: four prep groups, 64 dW windows). The
 # oracle checks sampled rows; dW is checked through identities that hold at
 # any size, computed on the GPU in float64.
 # --------------------------------------------------------------------------
