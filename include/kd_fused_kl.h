@@ -43,10 +43,11 @@
  *    on entry are irrelevant and on exit unspecified.
  *  - Invalid arguments are reported by the return value BEFORE anything is
  *    enqueued. A failed launch returns KD_ERR_HIP.
- *  - Preconditions not checked on the host: teacher ids are distinct within
- *    a row; logp values are <= 0 and finite or −inf (−inf means p = 0 and the
- *    entry contributes nothing). Ids outside [0, V) are skipped by the
- *    kernels (never dereferenced) and count as p = 0.
+ *  - Preconditions not checked on the hot path: teacher ids are distinct
+ *    within a row; logp values are <= 0 and finite or −inf (−inf means p = 0
+ *    and the entry contributes nothing). Ids outside [0, V) are skipped by
+ *    the kernels (never dereferenced) and count as p = 0.
+ *    kd_fused_kl_check_inputs checks all three on request.
  *  - Results are deterministic: every reduction runs in a fixed order.
  *  - Calls that share one workspace must not overlap.
  */
@@ -232,21 +233,24 @@ int kd_cast_f32_to_bf16(const float* src, void* dst, int64_t n, void* stream);
 /*
  * Kernel timing, for benchmarks. Not part of the loss.
  *
- * kd_timing_enable(1) makes every later fwd/bwd call bracket its kernel
- * launches with HIP events on the caller's stream (kd_timing_enable(0) stops
- * it). kd_timing_read waits for the recorded events, writes per kernel class
- * the summed milliseconds (total_ms[KD_KERNEL_CLASSES]) and launch counts
+ * kd_timing_enable(1) makes every later loss or teacher-cache call bracket
+ * its kernel launches with HIP events on the caller's stream
+ * (kd_timing_enable(0) stops it). kd_timing_read waits for the recorded
+ * events, writes per kernel class the summed milliseconds
+ * (total_ms[KD_KERNEL_CLASSES]) and launch counts
  * (launches[KD_KERNEL_CLASSES]), and clears the record. A "launch" of
- * KD_KERNEL_PREP is the three prep kernels of one chunk. Not thread-safe;
- * this is the one entry point that synchronises (with its own events).
+ * KD_KERNEL_PREP is the three prep kernels of one group of chunks, or the
+ * transpose of one chunk of H. The teacher cache's two GEMM passes count as
+ * KD_KERNEL_FWD_LOGITS. Global state, not thread-safe; this is the one entry
+ * point that synchronises (with its own events).
  */
 enum {
-  KD_KERNEL_PREP = 0,         /* bucket the chunk's top-K entries             */
+  KD_KERNEL_PREP = 0,         /* bucket top-K entries; transpose a chunk of H */
   KD_KERNEL_FWD_LOGITS = 1,   /* fused logit tile + logsumexp partials        */
   KD_KERNEL_BWD_DLOGITS = 2,  /* recomputed logit tile -> dlogits             */
   KD_KERNEL_BWD_DH = 3,       /* dH = dlogits W                               */
   KD_KERNEL_BWD_DW = 4,       /* dW (+)= dlogitsᵀ H                           */
-  KD_KERNEL_OTHER = 5,        /* combine, split reduce                        */
+  KD_KERNEL_OTHER = 5,        /* combine, split reduce, teacher select/finish */
   KD_KERNEL_CLASSES = 6
 };
 int kd_timing_enable(int enable);
