@@ -133,6 +133,17 @@ def test_neg_inf_logprob_contributes_nothing(kd):
     assert_parity(got, ref, "f32", "-inf")
 
 
+def test_permuting_cache_columns_changes_nothing(kd):
+    # The loss and gradients do not depend on the order of the K cached
+    # entries of a row; only the summation order (rounding) may change.
+    H, W, idx, logp = _case(200, 64, 900, 12, "f32", seed=8)
+    perm = torch.randperm(12, generator=torch.Generator().manual_seed(3))
+    a = run_hip(kd, H, W, idx, logp, 64)
+    b = run_hip(kd, H, W, idx[:, perm].contiguous(), logp[:, perm].contiguous(), 64)
+    assert rel_err(a["loss"], b["loss"]) < 1e-5 and rel_err(a["loss_tok"], b["loss_tok"]) < 1e-5
+    assert max_norm_err(a["dH"], b["dH"]) < 1e-5 and max_norm_err(a["dW"], b["dW"]) < 1e-5
+
+
 def test_teacher_equal_to_student_gives_zero_loss(kd):
     H, W, _, _ = _case(64, 32, 500, 8, "f32", seed=6)
     logq = torch.log_softmax(H.double() @ W.double().T, dim=1)
