@@ -1241,54 +1241,58 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
                          a);
     });
 
-    if (dH) {
-      DhArgs h;
-      h.W = ColOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
-      h.dl = RowOp{dl_c, dl_ld_bytes, rows, int(dl_ld_bytes)};
-      h.tiles_t = tiles_t;
-      h.tiles_d = int(cdiv(p.d, kBM));
-      h.splits = p.dh_splits;
-      h.kt_total = int(p.kt_v);
-      h.rows = rows;
-      h.d = int(p.d);
-      h.dH = static_cast<char*>(dH) + r0 * row_bytes;
-      h.part = p.dh_splits > 1 ? ws.at<float>(p.off_dhpart) : nullptr;
-      h.part_stride = p.C_pad * p.d;
-      timed(KD_KERNEL_BWD_DH, st, [&] {
-        hipLaunchKernelGGL(dh_kernel, dim3(h.tiles_t * h.tiles_d * h.splits), dim3(kThreads), 0, st,
-                           h);
-      });
-      if (p.dh_splits > 1) {
-        const int64_t n4 = int64_t(rows) * p.d / 4;
-        const int nb = int(cdiv(n4, 256) < 4096 ? cdiv(n4, 256) : 4096);
-        timed(KD_KERNEL_OTHER, st, [&] {
-          hipLaunchKernelGGL(k_bwd_dh_reduce<BF16>, dim3(nb), dim3(256), 0, st, h.part, h.splits,
-                             h.part_stride, n4, h.dH);
-        });
-      }
-    }
     ++win_chunks;
     const bool last = r0 + rows >= p.N;
-    if (dW && (win_chunks == p.dw_window || last)) {
-      // dW (+)= dlᵀ H over the window's rows, in chunk order.
+    if (win_chunks == p.dw_window || last) {
+      // The window's dlogits rows (its chunks, back to back) are complete.
       const int krows = int(r0 + rows - win_r0);
-      DwArgs w;
-      w.H = ColOp{static_cast<const char*>(H) + win_r0 * row_bytes, row_bytes, krows,
-                  int(row_bytes)};
-      w.dl = ColOp{ws.at<char>(p.off_dl), dl_ld_bytes, krows, int(dl_ld_bytes)};
-      w.tiles_d = int(cdiv(p.d, kBM));
-      w.tiles_v = int(cdiv(p.V, kBN));
-      w.kt = int(cdiv(krows, k_per_stage));
-      w.V = int(p.V);
-      w.d = int(p.d);
-      w.dW = dW;
-      w.beta = dw_written ? 1 : 0;
-      timed(KD_KERNEL_BWD_DW, st, [&] {
-        hipLaunchKernelGGL(dw_kernel, dim3(w.tiles_d * w.tiles_v), dim3(kThreads), 0, st, w);
-      });
-      dw_written = true;
+      if (dH) {
+        // dH of the window's rows = dl · W, split over the vocabulary.
+        DhArgs h;
+        h.W = ColOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
+        h.dl = RowOp{ws.at<char>(p.off_dl), dl_ld_bytes, krows, int(dl_ld_bytes)};
+        h.tiles_t = int(cdiv(krows, kBN));
+        h.tiles_d = int(cdiv(p.d, kBM));
+        h.splits = p.dh_splits;
+        h.kt_total = int(p.kt_v);
+        h.rows = krows;
+        h.d = int(p.d);
+        h.dH = static_cast<char*>(dH) + win_r0 * row_bytes;
+        h.part = p.dh_splits > 1 ? ws.at<float>(p.off_dhpart) : nullptr;
+        h.part_stride = p.win_rows_pad * p.d;
+        timed(KD_KERNEL_BWD_DH, st, [&] {
+          hipLaunchKernelGGL(dh_kernel, dim3(h.tiles_t * h.tiles_d * h.splits), dim3(kThreads), 0,
+                             st, h);
+        });
+        if (p.dh_splits > 1) {
+          const int64_t n4 = int64_t(krows) * p.d / 4;
+          const int nb = int(cdiv(n4, 256) < 4096 ? cdiv(n4, 256) : 4096);
+          timed(KD_KERNEL_OTHER, st, [&] {
+            hipLaunchKernelGGL(k_bwd_dh_reduce<BF16>, dim3(nb), dim3(256), 0, st, h.part, h.splits,
+                               h.part_stride, n4, h.dH);
+          });
+        }
+      }
+      if (dW) {
+        // dW (+)= dlᵀ H over the window's rows, in chunk order.
+        DwArgs w;
+        w.H = ColOp{static_cast<const char*>(H) + win_r0 * row_bytes, row_bytes, krows,
+                    int(row_bytes)};
+        w.dl = ColOp{ws.at<char>(p.off_dl), dl_ld_bytes, krows, int(dl_ld_bytes)};
+        w.tiles_d = int(cdiv(p.d, kBM));
+        w.tiles_v = int(cdiv(p.V, kBN));
+        w.kt = int(cdiv(krows, k_per_stage));
+        w.V = int(p.V);
+        w.d = int(p.d);
+        w.dW = dW;
+        w.beta = dw_written ? 1 : 0;
+        timed(KD_KERNEL_BWD_DW, st, [&] {
+          hipLaunchKernelGGL(dw_kernel, dim3(w.tiles_d * w.tiles_v), dim3(kThreads), 0, st, w);
+        });
+        dw_written = true;
+      }
+      win_chunks = 0;
     }
-    if (win_chunks == p.dw_window) win_chunks = 0;
   }
   return launch_status();
 }

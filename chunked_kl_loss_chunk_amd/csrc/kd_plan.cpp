@@ -52,20 +52,22 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
   if (q.V_pad * es * kTileM >= (int64_t(1) << 31) || d * es * kTileM >= (int64_t(1) << 31))
     return KD_ERR_UNSUPPORTED;
 
-  // dH = dlogits · W has a short output (C × d) and a long contraction (V):
-  // split the contraction so that enough workgroups exist to fill the chip.
-  const int64_t tiles_mn = q.nMt * cdiv(d, 256);
-  int64_t splits = cdiv(kDhTargetTiles, tiles_mn);
-  if (splits > kMaxDhSplits) splits = kMaxDhSplits;
-  if (splits > q.kt_v) splits = q.kt_v;
-  if (splits < 1) splits = 1;
-  q.dh_splits = static_cast<int>(splits);
   const int64_t n_chunks = N > 0 ? cdiv(N, q.C) : 1;
   int64_t window = kDwRows / q.C;
   if (window > kDwMaxWindow) window = kDwMaxWindow;
   if (window > n_chunks) window = n_chunks;
   if (window < 1) window = 1;
   q.dw_window = static_cast<int>(window);
+  // dH = dlogits · W of a window has a short output (window rows × d) and a
+  // long contraction (V): split the contraction so that enough workgroups
+  // exist to fill the chip.
+  q.win_rows_pad = cdiv(window * q.C, kTileM) * kTileM;
+  const int64_t tiles_mn = (q.win_rows_pad / kTileM) * cdiv(d, 256);
+  int64_t splits = cdiv(kDhTargetTiles, tiles_mn);
+  if (splits > kMaxDhSplits) splits = kMaxDhSplits;
+  if (splits > q.kt_v) splits = q.kt_v;
+  if (splits < 1) splits = 1;
+  q.dh_splits = static_cast<int>(splits);
   int64_t group = kPrepBuckets / q.nb;
   if (group > kPrepRows / q.C) group = kPrepRows / q.C;
   if (group > n_chunks) group = n_chunks;
@@ -105,7 +107,7 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
     // The window's chunks are packed back to back ([window·C][V_pad]); the
     // last tile of the last chunk may read (never write) up to C_pad rows.
     q.off_dl = take(size_t(es) * size_t((q.dw_window - 1) * q.C + q.C_pad) * size_t(q.V_pad));
-    q.off_dhpart = q.dh_splits > 1 ? take(sizeof(float) * size_t(q.dh_splits) * size_t(q.C_pad) *
+    q.off_dhpart = q.dh_splits > 1 ? take(sizeof(float) * size_t(q.dh_splits) * size_t(q.win_rows_pad) *
                                           size_t(d))
                                     : 0;
   }

@@ -20,7 +20,7 @@ constexpr int64_t kMaxK = (1 << 14) - 1;
 constexpr int64_t kMaxTeacherK = 2048;
 // Upper bound on the dH split-K factor.
 constexpr int kMaxDhSplits = 32;
-// Target number of dH workgroups per chunk (three waves of the 256 CUs).
+// Target number of dH workgroups per dW window (three waves of the 256 CUs).
 constexpr int kDhTargetTiles = 768;
 // The cached ids of a group of consecutive chunks are bucketed by one prep
 // pass: at most kPrepBuckets buckets and kPrepRows rows per group.
@@ -46,7 +46,8 @@ struct Plan {
   int64_t prep_chunks;  // chunks bucketed by one prep pass
   int64_t kt_d;   // stages along d   (d * es / kStageRowBytes, rounded up)
   int64_t kt_v;   // stages along V_pad
-  int dh_splits;  // split-K factor of the dH contraction
+  int dh_splits;  // split-K factor of the dH contraction (once per dW window)
+  int64_t win_rows_pad;  // rows of a full dW window, rounded up to kTileM
   int dw_window;  // chunks whose dlogits are held before one dW contraction
   // byte offsets inside the workspace (all 256-byte aligned)
   size_t off_counts, off_offsets, off_recs, off_rowS, off_zhit, off_part, off_loss, off_flag;
