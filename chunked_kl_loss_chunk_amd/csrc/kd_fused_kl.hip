@@ -1245,7 +1245,27 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
     const bool last = r0 + rows >= p.N;
     if (win_chunks == p.dw_window || last) {
       // The window's dlogits rows (its chunks, back to back) are complete.
+      // dW goes first: of two back-to-back heavy launches the second runs at
+      // a lower clock, and dH is the shorter one.
       const int krows = int(r0 + rows - win_r0);
+      if (dW) {
+        // dW (+)= dlᵀ H over the window's rows, in chunk order.
+        DwArgs w;
+        w.H = ColOp{static_cast<const char*>(H) + win_r0 * row_bytes, row_bytes, krows,
+                    int(row_bytes)};
+        w.dl = ColOp{ws.at<char>(p.off_dl), dl_ld_bytes, krows, int(dl_ld_bytes)};
+        w.tiles_d = int(cdiv(p.d, kBM));
+        w.tiles_v = int(cdiv(p.V, kBN));
+        w.kt = int(cdiv(krows, k_per_stage));
+        w.V = int(p.V);
+        w.d = int(p.d);
+        w.dW = dW;
+        w.beta = dw_written ? 1 : 0;
+        timed(KD_KERNEL_BWD_DW, st, [&] {
+          hipLaunchKernelGGL(dw_kernel, dim3(w.tiles_d * w.tiles_v), dim3(kThreads), 0, st, w);
+        });
+        dw_written = true;
+      }
       if (dH) {
         // dH of the window's rows = dl · W, split over the vocabulary.
         DhArgs h;
@@ -1272,24 +1292,6 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
                                h.part_stride, n4, h.dH);
           });
         }
-      }
-      if (dW) {
-        // dW (+)= dlᵀ H over the window's rows, in chunk order.
-        DwArgs w;
-        w.H = ColOp{static_cast<const char*>(H) + win_r0 * row_bytes, row_bytes, krows,
-                    int(row_bytes)};
-        w.dl = ColOp{ws.at<char>(p.off_dl), dl_ld_bytes, krows, int(dl_ld_bytes)};
-        w.tiles_d = int(cdiv(p.d, kBM));
-        w.tiles_v = int(cdiv(p.V, kBN));
-        w.kt = int(cdiv(krows, k_per_stage));
-        w.V = int(p.V);
-        w.d = int(p.d);
-        w.dW = dW;
-        w.beta = dw_written ? 1 : 0;
-        timed(KD_KERNEL_BWD_DW, st, [&] {
-          hipLaunchKernelGGL(dw_kernel, dim3(w.tiles_d * w.tiles_v), dim3(kThreads), 0, st, w);
-        });
-        dw_written = true;
       }
       win_chunks = 0;
     }
