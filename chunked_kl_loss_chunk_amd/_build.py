@@ -10,6 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libkdkl.so")
+CLIENT_SRC = os.path.join(PKG, "examples", "abi_client.cpp")
+CLIENT_PATH = os.path.join(PKG, "examples", "abi_client")
 SOURCES = ["kd_fused_kl.hip", "kd_plan.cpp"]
 HEADERS = ["kd_gemm.h", "kd_plan.h"]
 
@@ -46,6 +48,20 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
+    # A C++ caller of the ABI alone (no Python), built by the host compiler
+    # and linked against the library and the HIP runtime.
+    tmp = CLIENT_PATH + ".tmp"
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = [shutil.which("g++") or "g++", "-O2", "-std=c++17", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-I", os.path.join(rocm, "include"), CLIENT_SRC, "-o", tmp,
+           "-L", PKG, "-lkdkl", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/..", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, CLIENT_PATH)
     return LIB_PATH
 
 
