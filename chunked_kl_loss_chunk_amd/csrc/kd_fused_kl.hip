@@ -447,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd_logits(FwdArgs a) {
 }
 
 // One wave per token: lse_r from the tile partials (fixed order), then
-// L_r = Σ_k p_k logp_k − Σ_k p_k z_k + S_r lse_r.
+// L_r = Σ_k p_k (logp_k − z_k + lse_r).
 __global__ __launch_bounds__(256) void k_fwd_combine(const float2* __restrict__ part, int nVt,
                                                      const float* __restrict__ zhit,
                                                      const int* __restrict__ idx,
@@ -472,23 +472,20 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const float2* __restrict__ 
   const int* ir = idx + (r0 + row) * K;
   const float* lr = logp + (r0 + row) * K;
   const float* zr = zhit + int64_t(row) * K;
-  float A = 0.f, B = 0.f, S = 0.f;
+  // L_r = Σ_k p_k (logp_k − (z_k − lse)): the log-probability z − lse is
+  // formed per entry, so a large common offset of the logits cancels before
+  // the sum instead of between two large sums.
+  float L = 0.f;
   for (int k = lane; k < K; k += 64) {
     const int j = ir[k];
     const float lp = lr[k];
     const float p = __expf(lp);
-    if (j >= 0 && j < V && p > 0.f) {
-      S += p;
-      A += p * lp;
-      B += p * zr[k];
-    }
+    if (j >= 0 && j < V && p > 0.f) L += p * (lp - (zr[k] - lse));
   }
-  A = wave_sum(A);
-  B = wave_sum(B);
-  S = wave_sum(S);
+  L = wave_sum(L);
   if (lane == 0) {
     lse_out[r0 + row] = lse;
-    loss_out[r0 + row] = A - B + S * lse;
+    loss_out[r0 + row] = L;
   }
 }
 

@@ -144,6 +144,22 @@ def test_permuting_cache_columns_changes_nothing(kd):
     assert max_norm_err(a["dH"], b["dH"]) < 1e-5 and max_norm_err(a["dW"], b["dW"]) < 1e-5
 
 
+def test_large_common_logit_offset(kd):
+    # A feature column equal for every token adds the same constant (about
+    # 300) to every logit of a row; the loss, dH and dW do not change.
+    H, W, idx, logp = _case(160, 64, 900, 10, "f32", seed=12)
+    H2 = torch.cat([H, torch.full((160, 1), 17.25)], dim=1)
+    W2 = torch.cat([W, torch.full((900, 1), 17.25)], dim=1)
+    H2 = torch.nn.functional.pad(H2, (0, 3)).contiguous()  # keep rows 16-byte aligned
+    W2 = torch.nn.functional.pad(W2, (0, 3)).contiguous()
+    got = run_hip(kd, H2, W2, idx, logp, 64)
+    ref = oracle.fused_kl_reference(H2, W2, idx, logp)
+    assert rel_err(got["loss"], ref["loss"]) < 1e-4
+    assert rel_err(got["loss_tok"], ref["loss_tok"]) < 1e-4
+    assert max_norm_err(got["dH"][:, :64], ref["dH"][:, :64]) < 1e-3
+    assert max_norm_err(got["dW"][:, :64], ref["dW"][:, :64]) < 1e-3
+
+
 def test_teacher_equal_to_student_gives_zero_loss(kd):
     H, W, _, _ = _case(64, 32, 500, 8, "f32", seed=6)
     logq = torch.log_softmax(H.double() @ W.double().T, dim=1)
