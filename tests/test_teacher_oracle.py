@@ -121,3 +121,17 @@ def test_invalid_k_rejected():
         oracle.teacher_topk_reference(np.ones((1, 2)), np.ones((3, 2)), 4)
     with pytest.raises(ValueError):
         oracle.teacher_topk_reference(np.ones((1, 2)), np.ones((3, 2)), 0)
+
+
+def test_lse_and_logp_match_scipy():
+    import scipy.special as sps
+
+    rng = np.random.default_rng(54)
+    Ht = rng.standard_normal((5, 7)) * 3.0
+    Wt = rng.standard_normal((60, 7))
+    out = oracle.teacher_topk_reference(Ht, Wt, 9)
+    Z = Ht @ Wt.T
+    np.testing.assert_allclose(out["lse"], sps.logsumexp(Z, axis=1), rtol=1e-13)
+    full = sps.log_softmax(Z, axis=1)
+    np.testing.assert_allclose(out["logp"], np.take_along_axis(full, out["idx"].astype(np.int64), axis=1),
+                               rtol=1e-12, atol=1e-12)
