@@ -123,6 +123,17 @@ def test_edge_shapes(kd, N, d, V, K, dtype, chunk):
     assert_parity(got, ref, dtype, f"{N},{d},{V},{K},{dtype},{chunk}")
 
 
+@pytest.mark.parametrize("N,d,V,K,dtype,chunk", [
+    (1100, 96, 3000, 20, "bf16", 128),   # 9 chunks: dW/dH windows of 4, 4 and 1 chunk (76 rows)
+    (1536, 256, 8000, 32, "f32", 512),   # the fp32 column path (register transposes) over 3 chunks
+])
+def test_multiple_windows(kd, N, d, V, K, dtype, chunk):
+    H, W, idx, logp = _case(N, d, V, K, dtype, seed=N + d)
+    got = run_hip(kd, H, W, idx, logp, chunk, grad=1.3)
+    ref = oracle.fused_kl_reference(H, W, idx, logp, grad=1.3)
+    assert_parity(got, ref, dtype, f"{N},{d},{V},{K},{dtype},{chunk}")
+
+
 def test_neg_inf_logprob_contributes_nothing(kd):
     H, W, idx, logp = _case(96, 64, 700, 6, "f32", seed=5)
     logp = logp.clone()
@@ -326,7 +337,11 @@ def test_full_size_gpt_oss_head(kd):
 
 
 @pytest.mark.timeout(900)
-def test_full_size_longest_context(kd):
-    cfg = workload.config(4, N=workload.SWEEP_N[-1])
-    _full_size_check(kd, cfg, [0, 2047, 2048, 65535, 65536, 131071, 196608, cfg.N - 1])
+@pytest.mark.parametrize("N", [workload.SWEEP_N[0], workload.SWEEP_N[-1]])
+def test_full_size_long_context(kd, N):
+    cfg = workload.config(4, N=N)
+    extra = [0, 2047, 2048, 4095, 4096, N // 2, N - 1]
+    if N > 65536:
+        extra += [65535, 65536, 131071, 196608]  # prep-group boundaries
+    _full_size_check(kd, cfg, extra)
     torch.cuda.empty_cache()
