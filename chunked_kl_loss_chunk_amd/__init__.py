@@ -14,6 +14,7 @@ from .ops import (  # noqa: F401
     fused_kl,
     kl_backward,
     kl_forward,
+    kl_forward_backward,
     teacher_topk,
     workspace_bytes,
 )

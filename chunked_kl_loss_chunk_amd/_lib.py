@@ -12,7 +12,7 @@ from ._build import LIB_PATH
 
 KD_OK, KD_ERR_INVALID_ARG, KD_ERR_UNSUPPORTED, KD_ERR_WORKSPACE, KD_ERR_HIP = range(5)
 KD_F32, KD_BF16 = 0, 1
-KD_PASS_FWD, KD_PASS_BWD, KD_PASS_TEACHER = 0, 1, 2
+KD_PASS_FWD, KD_PASS_BWD, KD_PASS_TEACHER, KD_PASS_FWD_BWD = 0, 1, 2, 3
 KD_REDUCE_SUM, KD_REDUCE_MEAN = 0, 1
 KD_CHECK_ID_RANGE, KD_CHECK_DUPLICATE, KD_CHECK_LOGP = 1, 2, 4
 
@@ -29,6 +29,8 @@ SIGNATURES = {
                                 _vp, _vp, _vp, _vp, _sz, _vp]),
     "kd_fused_kl_bwd_ex": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _i64, _i64, _i64, _i64,
                                 _i64, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
+    "kd_fused_kl_fwd_bwd": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _i64, _i64, _i64, _i64, _i64,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
     "kd_teacher_topk": (_i, [_vp, _vp, _i, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz,
                              _vp]),
     "kd_fused_kl_check_inputs": (_i, [_vp, _vp, _i64, _i64, _i64, _vp, _vp]),
@@ -37,7 +39,7 @@ SIGNATURES = {
     "kd_timing_read": (_i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
 }
 
-KERNEL_CLASSES = ("prep", "fwd_logits", "bwd_dlogits", "bwd_dh", "bwd_dw", "other")
+KERNEL_CLASSES = ("prep", "fwd_logits", "bwd_dlogits", "bwd_dh", "bwd_dw", "other", "dl_stream")
 
 _LIB = None
 

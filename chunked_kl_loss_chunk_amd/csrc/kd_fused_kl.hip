@@ -290,6 +290,8 @@ struct FwdArgs {
   const uint2* recs;
   float* zhit;     // [C, K]: z at the cached ids
   float2* part;    // [C_pad, nVt]: (max, Σexp) of each token over each vocabulary tile
+  float* z;        // STORE_Z: the chunk's logits, [rows][ld_z] float32, token-major
+  int64_t ld_z;
 };
 
 // Hit records of one tile. The epilogue starts by loading the first 64
@@ -350,7 +352,10 @@ __device__ __forceinline__ float staged_at(const lds_f32* region, int wr, int wc
   return region[(wc & 31) * kColStride + wr];
 }
 
-template <bool BF16>
+// STORE_Z: the one-pass variant. Instead of gathering z at the cached ids it
+// writes the whole tile of logits (float32, token-major), and the cached ids
+// are read back from there per row.
+template <bool BF16, bool STORE_Z>
 __global__ __launch_bounds__(kThreads) void k_fwd_logits(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
   lds_t* smem = (lds_t*)(smem_raw);
@@ -368,8 +373,6 @@ __global__ __launch_bounds__(kThreads) void k_fwd_logits(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % kWM, wn = wave / kWM;
-
-  const TileHits hits = hits_begin(a.offsets, a.recs, tt * a.nVt + vt, lane);
 
   // Per token: max and Σexp over this tile's valid vocabulary rows.
   const int vlim = a.V - (v_base + wm * kWTM);  // rows of this wave below vlim are valid
@@ -413,9 +416,34 @@ __global__ __launch_bounds__(kThreads) void k_fwd_logits(FwdArgs a) {
     if (lane < 32) red[wm * kBN + acc_col(wn, b, lane)] = make_float2(m, s);
   }
 
-  // z at the cached teacher ids that fall in this tile, one column block at a time.
   lds_f32* region = reinterpret_cast<lds_f32*>(smem + kWM * kBN * sizeof(float2)) +
                     wave * (kStageBlockBytes / 4);
+  if constexpr (STORE_Z) {
+    // The tile leaves one 32-token column block at a time, staged in LDS as
+    // [token][vocabulary] and written as 16-byte pieces, each token's 128
+    // entries of this wave in one contiguous 512-byte run. Vocabulary rows
+    // past V hold 0 (zero-filled operand rows) and land in the row padding.
+    const int sub = lane >> 4, c8 = (lane & 15) * 8;  // 4 tokens × 16 lanes
+#pragma unroll
+    for (int b = 0; b < kTN; ++b) {
+      stage_block_column(acc, b, region, lane);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int tl = sub + 4 * j;
+        const int64_t tok = t_base + wn * kWTN + b * 32 + tl;
+        const lds_f32* src = region + tl * kColStride + c8;
+        const f32x4_t v0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(src);
+        const f32x4_t v1 =
+            *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(src + 4);
+        if (tok >= a.rows) continue;
+        float* dst = a.z + tok * a.ld_z + v_base + wm * kWTM + c8;
+        *reinterpret_cast<float4*>(dst) = make_float4(v0[0], v0[1], v0[2], v0[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(v1[0], v1[1], v1[2], v1[3]);
+      }
+    }
+  } else {
+  // z at the cached teacher ids that fall in this tile, one column block at a time.
+  const TileHits hits = hits_begin(a.offsets, a.recs, tt * a.nVt + vt, lane);
   for (int base = 0; base < hits.n; base += 64) {
     const uint2 r = hits_load(hits, base, lane);
     const uint64_t mine = hits_mine(hits, r, base, wm, wn, lane);
@@ -436,6 +464,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd_logits(FwdArgs a) {
       }
     }
   }
+  }
 
   __syncthreads();
   if (t_base + tid < a.rows) {
@@ -447,14 +476,19 @@ __global__ __launch_bounds__(kThreads) void k_fwd_logits(FwdArgs a) {
 }
 
 // One wave per token: lse_r from the tile partials (fixed order), then
-// L_r = Σ_k p_k (logp_k − z_k + lse_r).
+// L_r = Σ_k p_k (logp_k − z_k + lse_r). z_k comes from the gathered zhit
+// [C][K], or, when zhit is null, from the stored logits z [rows][ld_z]; a
+// non-null rowS also receives S_r = Σ_k p_k over the valid entries, summed
+// exactly as the prep pass sums it.
 __global__ __launch_bounds__(256) void k_fwd_combine(const float2* __restrict__ part, int nVt,
                                                      const float* __restrict__ zhit,
+                                                     const float* __restrict__ z, int64_t ld_z,
                                                      const int* __restrict__ idx,
                                                      const float* __restrict__ logp, int64_t r0,
                                                      int rows, int K, int V,
                                                      float* __restrict__ lse_out,
-                                                     float* __restrict__ loss_out) {
+                                                     float* __restrict__ loss_out,
+                                                     float* __restrict__ rowS) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
   float m = kNegInf, s = 0.f;
@@ -471,22 +505,108 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const float2* __restrict__ 
   const float lse = m + __logf(s);
   const int* ir = idx + (r0 + row) * K;
   const float* lr = logp + (r0 + row) * K;
-  const float* zr = zhit + int64_t(row) * K;
+  const float* zr = zhit ? zhit + int64_t(row) * K : nullptr;
+  const float* zrow = z + int64_t(row) * ld_z;
   // L_r = Σ_k p_k (logp_k − (z_k − lse)): the log-probability z − lse is
   // formed per entry, so a large common offset of the logits cancels before
   // the sum instead of between two large sums.
-  float L = 0.f;
+  float L = 0.f, S = 0.f;
   for (int k = lane; k < K; k += 64) {
     const int j = ir[k];
     const float lp = lr[k];
     const float p = __expf(lp);
-    if (j >= 0 && j < V && p > 0.f) L += p * (lp - (zr[k] - lse));
+    if (j >= 0 && j < V && p > 0.f) {
+      L += p * (lp - ((zr ? zr[k] : zrow[j]) - lse));
+      S += p;
+    }
   }
   L = wave_sum(L);
+  if (rowS) S = wave_sum(S);
   if (lane == 0) {
     lse_out[r0 + row] = lse;
     loss_out[r0 + row] = L;
+    if (rowS) rowS[row] = S;
   }
+}
+
+// --------------------------------------------------------------------------
+// one-pass loss and gradients: stored logits -> dlogits
+// --------------------------------------------------------------------------
+// dl = g w_r S_r exp(z − lse_r) for every vocabulary entry below V and 0 in
+// the row padding up to V_pad, with the same float32 expressions as the
+// recomputing dlogits kernel. A workgroup covers 8192 entries of one row:
+// each lane reads 16 bytes of logits per step (a wave: 1 KiB contiguous) and
+// writes 8 (bf16) or 16 (float32) bytes.
+constexpr int kDlGroups = 8;                             // 4-entry groups per lane
+constexpr int kDlCols = 256 * 4 * kDlGroups;             // entries per workgroup
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_dl_dense(const float* __restrict__ z, int64_t ld_z,
+                                                  const float* __restrict__ lse,
+                                                  const float* __restrict__ rowS,
+                                                  const float* __restrict__ grad,
+                                                  const float* __restrict__ w, int nseg, int V,
+                                                  int V_pad, void* __restrict__ dl_out,
+                                                  int64_t ld_dl) {
+  typedef typename Elt<BF16>::T T;
+  const int row = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+  const float g = *grad;
+  const float l = lse[row];
+  const float gs = g * (w ? w[row] : 1.f) * rowS[row];
+  const float* zr = z + int64_t(row) * ld_z;
+  T* dr = reinterpret_cast<T*>(dl_out) + int64_t(row) * ld_dl;
+  const int c0 = seg * kDlCols + threadIdx.x * 4;
+  float4 v[kDlGroups];
+#pragma unroll
+  for (int u = 0; u < kDlGroups; ++u) {
+    const int c = c0 + u * 1024;
+    v[u] = c < V_pad ? *reinterpret_cast<const float4*>(zr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int u = 0; u < kDlGroups; ++u) {
+    const int c = c0 + u * 1024;
+    if (c >= V_pad) continue;
+    float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = c + i < V ? gs * __expf(e[i] - l) : 0.f;
+    if constexpr (BF16) {
+      const auto pk = [](float lo, float hi) {
+        return uint32_t(__builtin_bit_cast(uint16_t, __bf16(lo))) |
+               (uint32_t(__builtin_bit_cast(uint16_t, __bf16(hi))) << 16);
+      };
+      *reinterpret_cast<uint2*>(dr + c) = make_uint2(pk(e[0], e[1]), pk(e[2], e[3]));
+    } else {
+      *reinterpret_cast<float4*>(dr + c) = make_float4(e[0], e[1], e[2], e[3]);
+    }
+  }
+}
+
+// The cached entries of the chunk, one lane each, launched after k_dl_dense:
+// dl at a cached id becomes g w_r (S_r q − p), formed in float32 from the
+// stored logit and rounded once, as in the recomputing dlogits kernel.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_dl_hits(const float* __restrict__ z, int64_t ld_z,
+                                                 const float* __restrict__ lse,
+                                                 const float* __restrict__ rowS,
+                                                 const float* __restrict__ grad,
+                                                 const float* __restrict__ w,
+                                                 const int* __restrict__ idx,
+                                                 const float* __restrict__ logp, int64_t r0,
+                                                 int rows, int K, int V, void* __restrict__ dl_out,
+                                                 int64_t ld_dl) {
+  typedef typename Elt<BF16>::T T;
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= int64_t(rows) * K) return;
+  const int row = int(i / K);
+  const int j = idx[r0 * K + i];
+  const float p = __expf(logp[r0 * K + i]);
+  if (!(j >= 0 && j < V && p > 0.f)) return;
+  const float g = *grad;
+  const float gs = g * (w ? w[row] : 1.f) * rowS[row];
+  const float gw = w ? g * w[row] : g;
+  // The product is rounded on its own before the fused correction, as it is
+  // when the recomputing kernel stages it in LDS.
+  const float v = __fmul_rn(gs, __expf(z[int64_t(row) * ld_z + j] - lse[row]));
+  reinterpret_cast<T*>(dl_out)[int64_t(row) * ld_dl + j] = T(__fmaf_rn(-gw, p, v));
 }
 
 // --------------------------------------------------------------------------
@@ -581,7 +701,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs a) {
         const float p = __uint_as_float(__builtin_amdgcn_readlane(r.y, j));
         const int tok = int(x & 255u), voc = int((x >> 8) & 1023u);
         const float gw = a.w ? g * a.w[t_base + tok] : g;
-        if (lane == 0) region[((tok - wn * kWTN) & 31) * kColStride + voc - wm * kWTM] -= gw * p;
+        lds_f32* cell = region + ((tok - wn * kWTN) & 31) * kColStride + voc - wm * kWTM;
+        if (lane == 0) *cell = __fmaf_rn(-gw, p, *cell);
       }
     }
 #pragma unroll
@@ -1171,18 +1292,79 @@ int run_fwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
       a.recs = ws.at<uint2>(p.off_recs);
       a.zhit = ws.at<float>(p.off_zhit);
       a.part = ws.at<float2>(p.off_part);
+      a.z = nullptr;
+      a.ld_z = 0;
       timed(KD_KERNEL_FWD_LOGITS, st, [&] {
-        hipLaunchKernelGGL(k_fwd_logits<BF16>, dim3(a.tiles_t * a.tiles_v), dim3(kThreads), 0, st,
-                           a);
+        hipLaunchKernelGGL((k_fwd_logits<BF16, false>), dim3(a.tiles_t * a.tiles_v),
+                           dim3(kThreads), 0, st, a);
       });
       timed(KD_KERNEL_OTHER, st, [&] {
         hipLaunchKernelGGL(k_fwd_combine, dim3(cdiv(rows, 4)), dim3(256), 0, st, a.part, a.nVt,
-                           a.zhit, idx, logp, r0, rows, a.K, a.V, lse, loss);
+                           a.zhit, nullptr, int64_t(0), idx, logp, r0, rows, a.K, a.V, lse, loss,
+                           nullptr);
       });
     }
   }
   hipLaunchKernelGGL(k_loss_reduce, dim3(1), dim3(1024), 0, st, loss, weight, p.N, mean, loss_sum);
   return launch_status();
+}
+
+// dW and dH of one window of chunks whose dlogits rows ([krows][V_pad], the
+// chunks back to back) are complete in the scratch. dW goes first: of two
+// back-to-back heavy launches the second runs at a lower clock, and dH is the
+// shorter one.
+template <bool BF16>
+void launch_window(const Plan& p, const Ws& ws, const void* H, const void* W, int64_t win_r0,
+                   int krows, void* dH, float* dW, bool& dw_written, hipStream_t st) {
+  const int64_t row_bytes = p.d * p.es;
+  const int64_t dl_ld_bytes = p.V_pad * p.es;
+  const int k_per_stage = kLdsRow / p.es;
+  if (dW) {
+    // dW (+)= dlᵀ H over the window's rows, in chunk order.
+    DwArgs w;
+    w.H = ColOp{static_cast<const char*>(H) + win_r0 * row_bytes, row_bytes, krows,
+                int(row_bytes)};
+    w.dl = ColOp{ws.at<char>(p.off_dl), dl_ld_bytes, krows, int(dl_ld_bytes)};
+    w.tiles_d = int(cdiv(p.d, kBM));
+    w.tiles_v = int(cdiv(p.V, kBN));
+    w.kt = int(cdiv(krows, k_per_stage));
+    w.V = int(p.V);
+    w.d = int(p.d);
+    w.dW = dW;
+    w.beta = dw_written ? 1 : 0;
+    timed(KD_KERNEL_BWD_DW, st, [&] {
+      hipLaunchKernelGGL((k_bwd_dw<BF16, ColLoad<BF16>>), dim3(w.tiles_d * w.tiles_v),
+                         dim3(kThreads), 0, st, w);
+    });
+    dw_written = true;
+  }
+  if (dH) {
+    // dH of the window's rows = dl · W, split over the vocabulary.
+    DhArgs h;
+    h.W = ColOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
+    h.dl = RowOp{ws.at<char>(p.off_dl), dl_ld_bytes, krows, int(dl_ld_bytes)};
+    h.tiles_t = int(cdiv(krows, kBN));
+    h.tiles_d = int(cdiv(p.d, kBM));
+    h.splits = p.dh_splits;
+    h.kt_total = int(p.kt_v);
+    h.rows = krows;
+    h.d = int(p.d);
+    h.dH = static_cast<char*>(dH) + win_r0 * row_bytes;
+    h.part = p.dh_splits > 1 ? ws.at<float>(p.off_dhpart) : nullptr;
+    h.part_stride = p.win_rows_pad * p.d;
+    timed(KD_KERNEL_BWD_DH, st, [&] {
+      hipLaunchKernelGGL((k_bwd_dh<BF16, ColLoad<BF16>>), dim3(h.tiles_t * h.tiles_d * h.splits),
+                         dim3(kThreads), 0, st, h);
+    });
+    if (p.dh_splits > 1) {
+      const int64_t n4 = int64_t(krows) * p.d / 4;
+      const int nb = int(cdiv(n4, 256) < 4096 ? cdiv(n4, 256) : 4096);
+      timed(KD_KERNEL_OTHER, st, [&] {
+        hipLaunchKernelGGL(k_bwd_dh_reduce<BF16>, dim3(nb), dim3(256), 0, st, h.part, h.splits,
+                           h.part_stride, n4, h.dH);
+      });
+    }
+  }
 }
 
 template <bool BF16>
@@ -1199,9 +1381,6 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
   float* const gscale = ws.at<float>(p.off_gscale);
   hipLaunchKernelGGL(k_grad_scale, dim3(1), dim3(1024), 0, st, grad, weight, p.N, mean, gscale);
   const int64_t row_bytes = p.d * p.es;
-  const int k_per_stage = kLdsRow / p.es;
-  auto dh_kernel = k_bwd_dh<BF16, ColLoad<BF16>>;
-  auto dw_kernel = k_bwd_dw<BF16, ColLoad<BF16>>;
   const int64_t dl_ld_bytes = p.V_pad * p.es;
   int64_t win_r0 = 0;   // first row of the current dW window
   int win_chunks = 0;   // chunks of the window held in the dlogits scratch
@@ -1241,58 +1420,90 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
     ++win_chunks;
     const bool last = r0 + rows >= p.N;
     if (win_chunks == p.dw_window || last) {
-      // The window's dlogits rows (its chunks, back to back) are complete.
-      // dW goes first: of two back-to-back heavy launches the second runs at
-      // a lower clock, and dH is the shorter one.
-      const int krows = int(r0 + rows - win_r0);
-      if (dW) {
-        // dW (+)= dlᵀ H over the window's rows, in chunk order.
-        DwArgs w;
-        w.H = ColOp{static_cast<const char*>(H) + win_r0 * row_bytes, row_bytes, krows,
-                    int(row_bytes)};
-        w.dl = ColOp{ws.at<char>(p.off_dl), dl_ld_bytes, krows, int(dl_ld_bytes)};
-        w.tiles_d = int(cdiv(p.d, kBM));
-        w.tiles_v = int(cdiv(p.V, kBN));
-        w.kt = int(cdiv(krows, k_per_stage));
-        w.V = int(p.V);
-        w.d = int(p.d);
-        w.dW = dW;
-        w.beta = dw_written ? 1 : 0;
-        timed(KD_KERNEL_BWD_DW, st, [&] {
-          hipLaunchKernelGGL(dw_kernel, dim3(w.tiles_d * w.tiles_v), dim3(kThreads), 0, st, w);
-        });
-        dw_written = true;
-      }
-      if (dH) {
-        // dH of the window's rows = dl · W, split over the vocabulary.
-        DhArgs h;
-        h.W = ColOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
-        h.dl = RowOp{ws.at<char>(p.off_dl), dl_ld_bytes, krows, int(dl_ld_bytes)};
-        h.tiles_t = int(cdiv(krows, kBN));
-        h.tiles_d = int(cdiv(p.d, kBM));
-        h.splits = p.dh_splits;
-        h.kt_total = int(p.kt_v);
-        h.rows = krows;
-        h.d = int(p.d);
-        h.dH = static_cast<char*>(dH) + win_r0 * row_bytes;
-        h.part = p.dh_splits > 1 ? ws.at<float>(p.off_dhpart) : nullptr;
-        h.part_stride = p.win_rows_pad * p.d;
-        timed(KD_KERNEL_BWD_DH, st, [&] {
-          hipLaunchKernelGGL(dh_kernel, dim3(h.tiles_t * h.tiles_d * h.splits), dim3(kThreads), 0,
-                             st, h);
-        });
-        if (p.dh_splits > 1) {
-          const int64_t n4 = int64_t(krows) * p.d / 4;
-          const int nb = int(cdiv(n4, 256) < 4096 ? cdiv(n4, 256) : 4096);
-          timed(KD_KERNEL_OTHER, st, [&] {
-            hipLaunchKernelGGL(k_bwd_dh_reduce<BF16>, dim3(nb), dim3(256), 0, st, h.part, h.splits,
-                               h.part_stride, n4, h.dH);
-          });
-        }
-      }
+      launch_window<BF16>(p, ws, H, W, win_r0, int(r0 + rows - win_r0), dH, dW, dw_written, st);
       win_chunks = 0;
     }
   }
+  return launch_status();
+}
+
+// Loss and gradients in one call. Per chunk: the logit GEMM stores the
+// chunk's logits (float32) besides its partials; the combine gives lse_r, L_r
+// and S_r; two streaming kernels turn the stored logits into the chunk's
+// dlogits rows; dW and dH follow per window of chunks as in the backward.
+template <bool BF16>
+int run_fwd_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, const float* logp,
+                const float* weight, int mean, const float* grad, float* loss_tok, float* lse,
+                float* loss_sum, void* dH, float* dW, int accumulate, void* workspace,
+                hipStream_t st) {
+  Ws ws{static_cast<char*>(workspace), p};
+  float* loss = loss_tok ? loss_tok : ws.at<float>(p.off_loss);
+  if (p.N == 0) {
+    if (dW && !accumulate)
+      hipLaunchKernelGGL(k_fill_f32, dim3(1024), dim3(256), 0, st, dW, p.V * p.d, 0.f);
+    hipLaunchKernelGGL(k_loss_reduce, dim3(1), dim3(1024), 0, st, loss, weight, p.N, mean,
+                       loss_sum);
+    return launch_status();
+  }
+  float* const gscale = ws.at<float>(p.off_gscale);
+  hipLaunchKernelGGL(k_grad_scale, dim3(1), dim3(1024), 0, st, grad, weight, p.N, mean, gscale);
+  const int64_t row_bytes = p.d * p.es;
+  const int64_t dl_ld_bytes = p.V_pad * p.es;
+  float* const z = ws.at<float>(p.off_z);
+  float* const rowS = ws.at<float>(p.off_rowS);
+  const int nseg = int(cdiv(p.V_pad, kDlCols));
+  int64_t win_r0 = 0;
+  int win_chunks = 0;
+  bool dw_written = accumulate != 0;
+  for (int64_t r0 = 0; r0 < p.N; r0 += p.C) {
+    const int rows = int(p.N - r0 < p.C ? p.N - r0 : p.C);
+    const char* Hc = static_cast<const char*>(H) + r0 * row_bytes;
+    if (win_chunks == 0) win_r0 = r0;
+    char* const dl_c = ws.at<char>(p.off_dl) + int64_t(win_chunks) * p.C * dl_ld_bytes;
+
+    FwdArgs a;
+    a.W = RowOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
+    a.H = RowOp{Hc, row_bytes, rows, int(row_bytes)};
+    a.Ht = BF16 ? chunk_transposed(p, ws, Hc, rows, st) : ColOp{};
+    a.kt = int(p.kt_d);
+    a.tiles_t = int(cdiv(rows, kBN));
+    a.tiles_v = int(p.nVt);
+    a.rows = rows;
+    a.V = int(p.V);
+    a.K = int(p.K);
+    a.nVt = int(p.nVt);
+    a.offsets = nullptr;
+    a.recs = nullptr;
+    a.zhit = nullptr;
+    a.part = ws.at<float2>(p.off_part);
+    a.z = z;
+    a.ld_z = p.V_pad;
+    timed(KD_KERNEL_FWD_LOGITS, st, [&] {
+      hipLaunchKernelGGL((k_fwd_logits<BF16, true>), dim3(a.tiles_t * a.tiles_v), dim3(kThreads),
+                         0, st, a);
+    });
+    timed(KD_KERNEL_OTHER, st, [&] {
+      hipLaunchKernelGGL(k_fwd_combine, dim3(cdiv(rows, 4)), dim3(256), 0, st, a.part, a.nVt,
+                         nullptr, z, p.V_pad, idx, logp, r0, rows, a.K, a.V, lse, loss, rowS);
+    });
+    const float* const wc = weight ? weight + r0 : nullptr;
+    timed(KD_KERNEL_DL_STREAM, st, [&] {
+      hipLaunchKernelGGL(k_dl_dense<BF16>, dim3(unsigned(int64_t(rows) * nseg)), dim3(256), 0, st,
+                         z, p.V_pad, lse + r0, rowS, gscale, wc, nseg, int(p.V), int(p.V_pad),
+                         dl_c, p.V_pad);
+      hipLaunchKernelGGL(k_dl_hits<BF16>, dim3(unsigned(cdiv(int64_t(rows) * p.K, 256))),
+                         dim3(256), 0, st, z, p.V_pad, lse + r0, rowS, gscale, wc, idx, logp, r0,
+                         rows, int(p.K), int(p.V), dl_c, p.V_pad);
+    });
+
+    ++win_chunks;
+    const bool last = r0 + rows >= p.N;
+    if (win_chunks == p.dw_window || last) {
+      launch_window<BF16>(p, ws, H, W, win_r0, int(r0 + rows - win_r0), dH, dW, dw_written, st);
+      win_chunks = 0;
+    }
+  }
+  hipLaunchKernelGGL(k_loss_reduce, dim3(1), dim3(1024), 0, st, loss, weight, p.N, mean, loss_sum);
   return launch_status();
 }
 
@@ -1322,9 +1533,11 @@ int run_teacher(const Plan& p, const void* Ht, const void* Wt, int32_t* idx, flo
     a.recs = ws.at<uint2>(p.off_recs);
     a.zhit = nullptr;  // never written: there are no cached ids
     a.part = ws.at<float2>(p.off_part);
+    a.z = nullptr;
+    a.ld_z = 0;
     timed(KD_KERNEL_FWD_LOGITS, st, [&] {
-      hipLaunchKernelGGL(k_fwd_logits<BF16>, dim3(a.tiles_t * a.tiles_v), dim3(kThreads), 0, st,
-                         a);
+      hipLaunchKernelGGL((k_fwd_logits<BF16, false>), dim3(a.tiles_t * a.tiles_v),
+                         dim3(kThreads), 0, st, a);
     });
     float* const lse_c = lse ? lse + r0 : ws.at<float>(p.off_lse);
     timed(KD_KERNEL_OTHER, st, [&] {
@@ -1445,6 +1658,38 @@ int kd_fused_kl_bwd_ex(const void* H, const void* W, int dtype, const int32_t* t
                                               grad_loss, dH, dW, dW_accumulate, workspace, s)
                           : kd::run_bwd<false>(p, H, W, topk_idx, topk_logp, weight, mean, lse,
                                                grad_loss, dH, dW, dW_accumulate, workspace, s);
+}
+
+int kd_fused_kl_fwd_bwd(const void* H, const void* W, int dtype, const int32_t* topk_idx,
+                        const float* topk_logp, const float* weight, int reduction, int64_t N,
+                        int64_t d, int64_t V, int64_t K, int64_t chunk, const float* grad_loss,
+                        float* loss_tok, float* lse, float* loss, void* dH, float* dW,
+                        int dW_accumulate, void* workspace, size_t workspace_bytes, void* stream) {
+  kd::Plan p;
+  const int st = kd::make_plan(KD_PASS_FWD_BWD, N, d, V, K, chunk, dtype, &p);
+  if (st != KD_OK) return st;
+  if (reduction != KD_REDUCE_SUM && reduction != KD_REDUCE_MEAN) return KD_ERR_INVALID_ARG;
+  if (dW_accumulate != 0 && dW_accumulate != 1) return KD_ERR_INVALID_ARG;
+  if (loss == nullptr || !kd::aligned(loss, 4)) return KD_ERR_INVALID_ARG;
+  if (dW && !kd::aligned(dW, 16)) return KD_ERR_INVALID_ARG;
+  if (N > 0) {
+    if (!H || !W || !topk_idx || !topk_logp || !lse || !grad_loss) return KD_ERR_INVALID_ARG;
+    if (!kd::aligned(H, 16) || !kd::aligned(W, 16) || !kd::aligned(topk_idx, 4) ||
+        !kd::aligned(topk_logp, 4) || !kd::aligned(lse, 4) || !kd::aligned(grad_loss, 4) ||
+        (loss_tok && !kd::aligned(loss_tok, 4)) || (dH && !kd::aligned(dH, 16)) ||
+        (weight && !kd::aligned(weight, 4)))
+      return KD_ERR_INVALID_ARG;
+  }
+  if (!workspace || !kd::aligned(workspace, 256) || workspace_bytes < p.total)
+    return KD_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float* w = N > 0 ? weight : nullptr;
+  const int mean = reduction == KD_REDUCE_MEAN;
+  return dtype == KD_BF16
+             ? kd::run_fwd_bwd<true>(p, H, W, topk_idx, topk_logp, w, mean, grad_loss, loss_tok,
+                                     lse, loss, dH, dW, dW_accumulate, workspace, s)
+             : kd::run_fwd_bwd<false>(p, H, W, topk_idx, topk_logp, w, mean, grad_loss, loss_tok,
+                                      lse, loss, dH, dW, dW_accumulate, workspace, s);
 }
 
 int kd_fused_kl_bwd(const void* H, const void* W, int dtype, const int32_t* topk_idx,

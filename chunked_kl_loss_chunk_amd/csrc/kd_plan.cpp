@@ -14,7 +14,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, int dtype,
               Plan* p) {
   if (p == nullptr) return KD_ERR_INVALID_ARG;
-  if (pass != KD_PASS_FWD && pass != KD_PASS_BWD && pass != KD_PASS_TEACHER)
+  if (pass != KD_PASS_FWD && pass != KD_PASS_BWD && pass != KD_PASS_TEACHER &&
+      pass != KD_PASS_FWD_BWD)
     return KD_ERR_INVALID_ARG;
   if (dtype != KD_F32 && dtype != KD_BF16) return KD_ERR_INVALID_ARG;
   if (N < 0 || d <= 0 || V <= 0 || K <= 0 || chunk <= 0) return KD_ERR_INVALID_ARG;
@@ -52,6 +53,10 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
   if (q.V_pad * es * kTileM >= (int64_t(1) << 31) || d * es * kTileM >= (int64_t(1) << 31))
     return KD_ERR_UNSUPPORTED;
 
+  // The one-pass streaming kernels run a workgroup per 8192 stored logits:
+  // keep their grids under 2^31 threads.
+  if (pass == KD_PASS_FWD_BWD && q.C * q.V_pad > (int64_t(1) << 36)) return KD_ERR_UNSUPPORTED;
+
   const int64_t n_chunks = N > 0 ? cdiv(N, q.C) : 1;
   int64_t window = kDwRows / q.C;
   if (window > kDwMaxWindow) window = kDwMaxWindow;
@@ -81,13 +86,22 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
     return o;
   };
   q.off_flag = take(256);
-  // Prep buffers of one group of chunks: bucket counts and offsets (chunk
-  // slot major), hit records, S_r.
-  q.off_counts = take(sizeof(int32_t) * size_t(q.prep_chunks * q.nb));
-  q.off_offsets = take(sizeof(int32_t) * size_t(q.prep_chunks * q.nb + 1));
-  q.off_recs = take(8 * size_t(q.prep_chunks * q.C * K));
-  q.off_rowS = take(sizeof(float) * size_t(q.prep_chunks * q.C));
+  if (pass == KD_PASS_FWD_BWD) {
+    // No buckets: the logits of a chunk are stored, so the cached entries are
+    // read per row. S_r of one chunk.
+    q.prep_chunks = 1;
+    q.off_counts = q.off_offsets = q.off_recs = 0;
+    q.off_rowS = take(sizeof(float) * size_t(q.C));
+  } else {
+    // Prep buffers of one group of chunks: bucket counts and offsets (chunk
+    // slot major), hit records, S_r.
+    q.off_counts = take(sizeof(int32_t) * size_t(q.prep_chunks * q.nb));
+    q.off_offsets = take(sizeof(int32_t) * size_t(q.prep_chunks * q.nb + 1));
+    q.off_recs = take(8 * size_t(q.prep_chunks * q.C * K));
+    q.off_rowS = take(sizeof(float) * size_t(q.prep_chunks * q.C));
+  }
   q.off_ht = dtype == KD_BF16 ? take(size_t(es) * size_t(d) * size_t(q.C_pad)) : 0;
+  q.off_z = 0;
   if (pass == KD_PASS_TEACHER) {
     // No cached ids: the bucket offsets stay zero, so the logit kernel sees
     // empty hit lists. Candidates: up to V_pad per row, so none overflows.
@@ -102,7 +116,15 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
     q.off_loss = take(sizeof(float) * size_t(N > 0 ? N : 1));
     q.off_dl = q.off_dhpart = 0;
   } else {
-    q.off_zhit = q.off_part = q.off_loss = 0;
+    q.off_zhit = 0;
+    q.off_part = q.off_loss = 0;
+    if (pass == KD_PASS_FWD_BWD) {
+      // Forward side: tile partials, per-row losses, and the chunk's logits
+      // in float32 ([C][V_pad]), kept until its dlogits are formed.
+      q.off_part = take(8 * size_t(q.C_pad * q.nVt));
+      q.off_loss = take(sizeof(float) * size_t(N > 0 ? N : 1));
+      q.off_z = take(sizeof(float) * size_t(q.C) * size_t(q.V_pad));
+    }
     q.off_gscale = take(256);
     // The window's chunks are packed back to back ([window·C][V_pad]); the
     // last tile of the last chunk may read (never write) up to C_pad rows.

@@ -56,10 +56,13 @@ struct Plan {
   size_t off_gscale;  // backward: the device scalar g (sum) or g / Σw (mean)
   // teacher cache producer: per-row lse, threshold, candidate count, candidates
   size_t off_lse, off_tau, off_cnt, off_cand;
+  // one-pass loss and gradients: the chunk's float32 logits, [C][V_pad]
+  size_t off_z;
   size_t total;
 };
 
-// Fills *p for the given pass (0 forward, 1 backward, 2 teacher cache).
+// Fills *p for the given pass (0 forward, 1 backward, 2 teacher cache,
+// 3 loss and gradients in one call).
 // Returns a kd_status.
 int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, int dtype,
               Plan* p);

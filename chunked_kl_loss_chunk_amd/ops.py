@@ -146,6 +146,50 @@ def kl_backward(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, logp: torch
     return dH, dW
 
 
+def kl_forward_backward(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor,
+                        logp: torch.Tensor, chunk: int, grad: Optional[torch.Tensor] = None,
+                        want_loss_tok: bool = True, need_dH: bool = True, need_dW: bool = True,
+                        dW_out: Optional[torch.Tensor] = None, accumulate: bool = False,
+                        weight: Optional[torch.Tensor] = None, reduction: str = "sum"):
+    """Loss and gradients in one call (kd_fused_kl_fwd_bwd): each chunk's
+    logits are projected once and kept only until its dlogits are formed.
+
+    Returns (loss [1], loss_tok [N] or None, lse [N], dH or None, dW or None),
+    the results of kl_forward followed by kl_backward with the same
+    arguments. ``grad`` (∂objective/∂loss, a 1-element fp32 tensor) defaults
+    to 1.
+    """
+    N, d, V, K = _check_inputs(H, W, idx, logp)
+    dev = H.device
+    dt = dtype_code(H.dtype)
+    red = _reduction(reduction)
+    weight = _check_weight(weight, N, dev)
+    if grad is None:
+        grad = torch.ones(1, dtype=torch.float32, device=dev)
+    grad = grad.reshape(1).to(device=dev, dtype=torch.float32).contiguous()
+    ws_n = workspace_bytes(_lib.KD_PASS_FWD_BWD, N, d, V, K, chunk, H.dtype)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    loss_tok = torch.empty(N, dtype=torch.float32, device=dev) if want_loss_tok else None
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    dH = torch.empty((N, d), dtype=H.dtype, device=dev) if need_dH else None
+    dW = None
+    if need_dW:
+        if dW_out is not None:
+            if dW_out.shape != (V, d) or dW_out.dtype != torch.float32 or not dW_out.is_contiguous():
+                raise ValueError("dW_out must be a contiguous fp32 [V,d] tensor")
+            dW = dW_out
+        else:
+            dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+            accumulate = False
+    st = _lib.lib().kd_fused_kl_fwd_bwd(_p(H), _p(W), dt, _p(idx), _p(logp), _p(weight), red, N,
+                                         d, V, K, chunk, _p(grad), _p(loss_tok), _p(lse),
+                                         _p(loss), _p(dH), _p(dW), 1 if accumulate else 0, _p(ws),
+                                         ws_n, _stream(dev))
+    _lib.check("kd_fused_kl_fwd_bwd", st)
+    return loss, loss_tok, lse, dH, dW
+
+
 def teacher_topk(Ht: torch.Tensor, Wt: torch.Tensor, K: int, chunk: int = 1024
                  ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Offline teacher cache of every row: (topk_idx int32 [N,K], topk_logp

@@ -74,7 +74,12 @@ typedef enum {
 typedef enum { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
 
 /* Which pass a workspace query is for. */
-typedef enum { KD_PASS_FWD = 0, KD_PASS_BWD = 1, KD_PASS_TEACHER = 2 } kd_pass;
+typedef enum {
+  KD_PASS_FWD = 0,
+  KD_PASS_BWD = 1,
+  KD_PASS_TEACHER = 2,
+  KD_PASS_FWD_BWD = 3 /* kd_fused_kl_fwd_bwd: loss and gradients in one call */
+} kd_pass;
 
 /* How per-position losses are accumulated (the _ex entry points). */
 typedef enum { KD_REDUCE_SUM = 0, KD_REDUCE_MEAN = 1 } kd_reduction;
@@ -83,14 +88,17 @@ typedef enum { KD_REDUCE_SUM = 0, KD_REDUCE_MEAN = 1 } kd_reduction;
 const char* kd_status_str(int status);
 
 /*
- * Bytes of workspace kd_fused_kl_fwd (pass = KD_PASS_FWD) or kd_fused_kl_bwd
- * (pass = KD_PASS_BWD) needs for these sizes. Returns 0 if the sizes are
+ * Bytes of workspace kd_fused_kl_fwd (pass = KD_PASS_FWD), kd_fused_kl_bwd
+ * (pass = KD_PASS_BWD), kd_teacher_topk (KD_PASS_TEACHER) or
+ * kd_fused_kl_fwd_bwd (KD_PASS_FWD_BWD) needs for these sizes. Returns 0 if the sizes are
  * invalid (the same checks the entry points make). The backward workspace
  * holds the dlogits of a window of consecutive chunks, window × chunk × V
  * elements of `dtype` (padded to the kernel tile), where the window is
  * min(4, max(1, 4096 / chunk)) chunks; dW is contracted once per window. It
- * grows with the chunk, never with N × V. Both passes also bucket the cached
- * entries of up to 65,536 positions at a time (about 8·K bytes per position).
+ * grows with the chunk, never with N × V. The forward and backward passes
+ * also bucket the cached entries of up to 65,536 positions at a time (about
+ * 8·K bytes per position). KD_PASS_FWD_BWD needs the backward's window and
+ * one chunk of float32 logits (chunk × V × 4 bytes), and no buckets.
  */
 size_t kd_fused_kl_workspace_bytes(int pass, int64_t N, int64_t d, int64_t V, int64_t K,
                                    int64_t chunk, int dtype);
@@ -175,6 +183,39 @@ int kd_fused_kl_bwd_ex(const void* H, const void* W, int dtype, const int32_t* t
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Loss and gradients in one call, for callers that know the upstream
+ * gradient g when they compute the loss (g = 1 for a loss that is the
+ * objective, or a fixed scale).
+ *
+ * The two-pass calls above follow the pages' schedule: the forward discards
+ * each chunk's logits and the backward recomputes them ("Distilação de LLMs
+ * mais barata ...", section "As duas mudanças": the projection is done twice).
+ * Here each chunk's logits are projected once. They are kept in float32 in
+ * the workspace only until that chunk's lse is known, turned into dlogits by
+ * a streaming pass, and then discarded. The workspace grows by chunk × V × 4
+ * bytes, still never with N × V, and the logit GEMM runs three times per
+ * chunk instead of four.
+ *
+ * The result equals kd_fused_kl_fwd_ex followed by kd_fused_kl_bwd_ex with
+ * the same arguments: the same logits, lse, losses and reductions, and the
+ * dlogits formed by the same float32 expressions. Arguments are those of the
+ * two calls:
+ *  - loss_tok, lse and loss as in kd_fused_kl_fwd_ex (lse is still written);
+ *  - grad_loss, dH, dW and dW_accumulate as in kd_fused_kl_bwd_ex.
+ * The workspace is kd_fused_kl_workspace_bytes(KD_PASS_FWD_BWD, ...). The
+ * errors are those of the two calls.
+ *
+ * Duplicate ids within a row are outside the contract, as for every entry
+ * point. Here the dlogits entry at a duplicated id keeps one of the
+ * duplicates' corrections, where the two-pass backward subtracts all of them.
+ */
+int kd_fused_kl_fwd_bwd(const void* H, const void* W, int dtype, const int32_t* topk_idx,
+                        const float* topk_logp, const float* weight, int reduction, int64_t N,
+                        int64_t d, int64_t V, int64_t K, int64_t chunk, const float* grad_loss,
+                        float* loss_tok, float* lse, float* loss, void* dH, float* dW,
+                        int dW_accumulate, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The offline teacher cache: run the teacher's output head once and keep,
  * for every position, the K most probable tokens with their log-probabilities
  * under the full softmax, not renormalised. Sources:
@@ -241,7 +282,8 @@ int kd_cast_f32_to_bf16(const float* src, void* dst, int64_t n, void* stream);
  * (launches[KD_KERNEL_CLASSES]), and clears the record. A "launch" of
  * KD_KERNEL_PREP is the three prep kernels of one group of chunks, or the
  * transpose of one chunk of H. The teacher cache's two GEMM passes count as
- * KD_KERNEL_FWD_LOGITS. Global state, not thread-safe; this is the one entry
+ * KD_KERNEL_FWD_LOGITS, and so does the logit pass of kd_fused_kl_fwd_bwd,
+ * which also stores the logits. Global state, not thread-safe; this is the one entry
  * point that synchronises (with its own events).
  */
 enum {
@@ -251,7 +293,8 @@ enum {
   KD_KERNEL_BWD_DH = 3,       /* dH = dlogits W                               */
   KD_KERNEL_BWD_DW = 4,       /* dW (+)= dlogitsᵀ H                           */
   KD_KERNEL_OTHER = 5,        /* combine, split reduce, teacher select/finish */
-  KD_KERNEL_CLASSES = 6
+  KD_KERNEL_DL_STREAM = 6,    /* kd_fused_kl_fwd_bwd: stored logits -> dlogits */
+  KD_KERNEL_CLASSES = 7
 };
 int kd_timing_enable(int enable);
 int kd_timing_read(double* total_ms, int64_t* launches);

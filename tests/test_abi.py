@@ -59,7 +59,8 @@ def test_workspace_size_rules(L):
     assert _ws(L, f, 128, 63, 1000, 8, 32, f32) == 0  # 63*4 bytes is not a multiple of 16
     assert _ws(L, f, 128, 68, 1000, 8, 32, bf) == 0   # 68*2 bytes is not a multiple of 16
     assert _ws(L, f, 128, 64, 1000, 8, 32, 7) == 0
-    assert _ws(L, 3, 128, 64, 1000, 8, 32, f32) == 0  # passes: 0 fwd, 1 bwd, 2 teacher
+    assert _ws(L, 4, 128, 64, 1000, 8, 32, f32) == 0  # passes: 0 fwd, 1 bwd, 2 teacher, 3 fwd+bwd
+    assert _ws(L, -1, 128, 64, 1000, 8, 32, f32) == 0
     assert _ws(L, f, 128, 64, 100000, 20000, 32, f32) == 0  # K beyond the record format
     # valid
     wf = _ws(L, f, 8192, 3072, 128256, 100, 1024, bf)
@@ -223,7 +224,7 @@ def test_teacher_workspace_holds_candidate_lists(L):
     assert n >= 1024 * 128256 * 8  # up to V candidates of 8 bytes per row of a chunk
     assert ws(_lib.KD_PASS_TEACHER, 4096, 4096, 128256, 2048, 1024, _lib.KD_BF16) > 0
     assert ws(_lib.KD_PASS_TEACHER, 4096, 4096, 128256, 2049, 1024, _lib.KD_BF16) == 0
-    assert ws(3, 4096, 4096, 128256, 100, 1024, _lib.KD_BF16) == 0
+    assert ws(4, 4096, 4096, 128256, 100, 1024, _lib.KD_BF16) == 0
 
 
 @pytest.mark.parametrize("args,want", [
@@ -236,3 +237,54 @@ def test_check_inputs_rejects_invalid(L, args, want):
     vp = ctypes.c_void_p
     idx, logp, N, K, V, flags = args
     assert L.kd_fused_kl_check_inputs(vp(idx), vp(logp), N, K, V, vp(flags), None) == want
+
+
+def test_one_pass_workspace(L):
+    """The one-pass call holds the backward's dlogits window plus one chunk of
+    float32 logits, and no bucketed cache: constant in N past the window."""
+    ws = L.kd_fused_kl_workspace_bytes
+    bf, o, b = _lib.KD_BF16, _lib.KD_PASS_FWD_BWD, _lib.KD_PASS_BWD
+    V_pad = (128256 + 255) // 256 * 256
+    w1 = ws(o, 8192, 3072, 128256, 100, 1024, bf)
+    assert w1 > 0 and w1 % 256 == 0
+    assert w1 >= 1024 * V_pad * 4 + 4 * 1024 * V_pad * 2
+    # no prep buckets: beyond the per-position loss buffer (4 bytes a row),
+    # the size does not grow with N
+    w2 = ws(o, 262144, 3072, 128256, 100, 1024, bf)
+    assert 0 <= w2 - w1 <= 4 * (262144 - 8192) + 256
+    # the extra over the backward is the chunk's logits (and small per-chunk buffers)
+    wb = ws(b, 8192, 3072, 128256, 100, 1024, bf)
+    assert 1024 * V_pad * 4 - (8 * 100 * 8192 + (1 << 22)) < w1 - wb <= 1024 * V_pad * 4 + (1 << 23)
+    # the streaming kernels' grid bound: chunk x V_pad <= 2^36
+    assert ws(o, 1 << 20, 64, 1 << 16, 8, 1 << 20, _lib.KD_F32) > 0
+    assert ws(o, 1 << 21, 64, 1 << 16, 8, 1 << 21, _lib.KD_F32) == 0
+    for pass_ in (0, 1, 2):
+        assert ws(pass_, 1 << 21, 64, 1 << 16, 8, 1 << 21, _lib.KD_F32) > 0
+
+
+def _fb(L, **kw):
+    a = dict(H=FAKE, W=FAKE, dt=_lib.KD_F32, idx=FAKE, logp=FAKE, w=None, red=0, N=128, d=64,
+             V=1000, K=8, C=32, grad=FAKE, loss_tok=FAKE, lse=FAKE, loss=FAKE, dH=FAKE, dW=FAKE,
+             acc=0, ws=FAKE, ws_n=1 << 40, stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return L.kd_fused_kl_fwd_bwd(vp(a["H"]), vp(a["W"]), a["dt"], vp(a["idx"]), vp(a["logp"]),
+                                 vp(a["w"]), a["red"], a["N"], a["d"], a["V"], a["K"], a["C"],
+                                 vp(a["grad"]), vp(a["loss_tok"]), vp(a["lse"]), vp(a["loss"]),
+                                 vp(a["dH"]), vp(a["dW"]), a["acc"], vp(a["ws"]), a["ws_n"],
+                                 a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(N=-1), INV), (dict(d=0), INV), (dict(V=0), INV), (dict(K=0), INV), (dict(K=1001), INV),
+    (dict(C=0), INV), (dict(dt=2), INV), (dict(d=63), INV), (dict(red=2), INV), (dict(acc=2), INV),
+    (dict(K=20000, V=100000), UNS), (dict(V=1 << 22), UNS),
+    (dict(H=None), INV), (dict(W=None), INV), (dict(idx=None), INV), (dict(logp=None), INV),
+    (dict(lse=None), INV), (dict(loss=None), INV), (dict(grad=None), INV),
+    (dict(H=FAKE + 8), INV), (dict(idx=FAKE + 2), INV), (dict(loss_tok=FAKE + 1), INV),
+    (dict(loss=FAKE + 2), INV), (dict(grad=FAKE + 2), INV), (dict(dH=FAKE + 8), INV),
+    (dict(dW=FAKE + 4), INV), (dict(w=FAKE + 2), INV),
+    (dict(ws=None), WSE), (dict(ws=FAKE + 16), WSE), (dict(ws_n=1024), WSE),
+])
+def test_one_pass_rejects_invalid(L, kw, want):
+    assert _fb(L, **kw) == want
