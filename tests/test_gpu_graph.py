@@ -52,3 +52,44 @@ def test_graph_replays_equal_eager(kd, dtype, weighted):
         torch.cuda.synchronize()
         for name, a, b in zip(("loss", "loss_tok", "lse", "dH", "dW"), outs, ref):
             assert torch.equal(a, b), (rep, name)
+
+
+def _eager_one_pass(kd, H, W, idx, logp, chunk, weight=None, reduction="sum"):
+    g = torch.full((1,), 0.75, dtype=torch.float32, device=H.device)
+    return kd.kl_forward_backward(H, W, idx, logp, chunk, grad=g, weight=weight,
+                                  reduction=reduction)
+
+
+@pytest.mark.parametrize("dtype,weighted", [("bf16", True), ("f32", False)])
+def test_one_pass_graph_replays_equal_eager(kd, dtype, weighted):
+    """kd_fused_kl_fwd_bwd captured once; each replay on new inputs equals an
+    eager call on them bit for bit."""
+    dev = torch.device("cuda:0")
+    N, d, V, K, chunk = 700, 96, 3000, 20, 128
+    H, W, idx, logp = (t.to(dev) for t in _case(N, d, V, K, dtype, seed=81))
+    w = torch.rand(N, device=dev) if weighted else None
+    red = "mean" if weighted else "sum"
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            _eager_one_pass(kd, H, W, idx, logp, chunk, w, red)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = _eager_one_pass(kd, H, W, idx, logp, chunk, w, red)
+    for rep in range(3):
+        Hn, Wn, idn, lpn = (t.to(dev) for t in _case(N, d, V, K, dtype, seed=82 + rep))
+        H.copy_(Hn)
+        W.copy_(Wn)
+        idx.copy_(idn)
+        logp.copy_(lpn)
+        if weighted:
+            w.copy_(torch.rand(N, device=dev))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = _eager_one_pass(kd, H, W, idx, logp, chunk, w, red)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("loss", "loss_tok", "lse", "dH", "dW"), outs, ref):
+            assert torch.equal(a, b), (rep, name)
