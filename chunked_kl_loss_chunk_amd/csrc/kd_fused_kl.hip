@@ -352,6 +352,62 @@ __device__ __forceinline__ float staged_at(const lds_f32* region, int wr, int wc
   return region[(wc & 31) * kColStride + wr];
 }
 
+// The forward tile's epilogue, one-pass variant: the tile leaves one 32-token
+// column block at a time, staged in LDS as [token][vocabulary] and written as
+// 16-byte pieces, each token's 128 entries of this wave in one contiguous
+// 512-byte run. Vocabulary rows past V hold 0 (zero-filled operand rows) and
+// land in the row padding.
+__device__ __forceinline__ void store_tile_logits(const Acc& acc, lds_f32* region,
+                                                  const FwdArgs& a, int t_base, int v_base, int wm,
+                                                  int wn, int lane) {
+  const int sub = lane >> 4, c8 = (lane & 15) * 8;  // 4 tokens × 16 lanes
+#pragma unroll
+  for (int b = 0; b < kTN; ++b) {
+    stage_block_column(acc, b, region, lane);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tl = sub + 4 * j;
+      const int64_t tok = t_base + wn * kWTN + b * 32 + tl;
+      const lds_f32* src = region + tl * kColStride + c8;
+      const f32x4_t v0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(src);
+      const f32x4_t v1 =
+          *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(src + 4);
+      if (tok >= a.rows) continue;
+      float* dst = a.z + tok * a.ld_z + v_base + wm * kWTM + c8;
+      *reinterpret_cast<float4*>(dst) = make_float4(v0[0], v0[1], v0[2], v0[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(v1[0], v1[1], v1[2], v1[3]);
+    }
+  }
+}
+
+// The forward tile's epilogue, two-pass variant: z at the cached teacher ids
+// that fall in this tile (bucket `bkt`), one column block at a time.
+__device__ __forceinline__ void gather_hit_logits(const Acc& acc, lds_f32* region,
+                                                  const FwdArgs& a, int bkt, int t_base, int wm,
+                                                  int wn, int lane) {
+  const TileHits hits = hits_begin(a.offsets, a.recs, bkt, lane);
+  for (int base = 0; base < hits.n; base += 64) {
+    const uint2 r = hits_load(hits, base, lane);
+    const uint64_t mine = hits_mine(hits, r, base, wm, wn, lane);
+    if (mine == 0) continue;
+#pragma unroll
+    for (int b = 0; b < kTN; ++b) {
+      const int wc_lane = int(r.x & 255u) - wn * kWTN;
+      uint64_t mask = mine & __ballot((wc_lane >> 5) == b);
+      if (mask == 0) continue;
+      stage_block_column(acc, b, region, lane);
+      while (mask) {
+        const int j = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        const uint32_t x = __builtin_amdgcn_readlane(r.x, j);
+        const int tok = int(x & 255u), voc = int((x >> 8) & 1023u), k = int(x >> 18);
+        const float z = staged_at(region, voc - wm * kWTM, tok - wn * kWTN);
+        if (lane == 0) a.zhit[int64_t(t_base + tok) * a.K + k] = z;
+      }
+    }
+  }
+}
+
 // STORE_Z: the one-pass variant. Instead of gathering z at the cached ids it
 // writes the whole tile of logits (float32, token-major), and the cached ids
 // are read back from there per row.
@@ -418,53 +474,10 @@ __global__ __launch_bounds__(kThreads) void k_fwd_logits(FwdArgs a) {
 
   lds_f32* region = reinterpret_cast<lds_f32*>(smem + kWM * kBN * sizeof(float2)) +
                     wave * (kStageBlockBytes / 4);
-  if constexpr (STORE_Z) {
-    // The tile leaves one 32-token column block at a time, staged in LDS as
-    // [token][vocabulary] and written as 16-byte pieces, each token's 128
-    // entries of this wave in one contiguous 512-byte run. Vocabulary rows
-    // past V hold 0 (zero-filled operand rows) and land in the row padding.
-    const int sub = lane >> 4, c8 = (lane & 15) * 8;  // 4 tokens × 16 lanes
-#pragma unroll
-    for (int b = 0; b < kTN; ++b) {
-      stage_block_column(acc, b, region, lane);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int tl = sub + 4 * j;
-        const int64_t tok = t_base + wn * kWTN + b * 32 + tl;
-        const lds_f32* src = region + tl * kColStride + c8;
-        const f32x4_t v0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(src);
-        const f32x4_t v1 =
-            *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(src + 4);
-        if (tok >= a.rows) continue;
-        float* dst = a.z + tok * a.ld_z + v_base + wm * kWTM + c8;
-        *reinterpret_cast<float4*>(dst) = make_float4(v0[0], v0[1], v0[2], v0[3]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(v1[0], v1[1], v1[2], v1[3]);
-      }
-    }
-  } else {
-  // z at the cached teacher ids that fall in this tile, one column block at a time.
-  const TileHits hits = hits_begin(a.offsets, a.recs, tt * a.nVt + vt, lane);
-  for (int base = 0; base < hits.n; base += 64) {
-    const uint2 r = hits_load(hits, base, lane);
-    const uint64_t mine = hits_mine(hits, r, base, wm, wn, lane);
-    if (mine == 0) continue;
-#pragma unroll
-    for (int b = 0; b < kTN; ++b) {
-      const int wc_lane = int(r.x & 255u) - wn * kWTN;
-      uint64_t mask = mine & __ballot((wc_lane >> 5) == b);
-      if (mask == 0) continue;
-      stage_block_column(acc, b, region, lane);
-      while (mask) {
-        const int j = __builtin_ctzll(mask);
-        mask &= mask - 1;
-        const uint32_t x = __builtin_amdgcn_readlane(r.x, j);
-        const int tok = int(x & 255u), voc = int((x >> 8) & 1023u), k = int(x >> 18);
-        const float z = staged_at(region, voc - wm * kWTM, tok - wn * kWTN);
-        if (lane == 0) a.zhit[int64_t(t_base + tok) * a.K + k] = z;
-      }
-    }
-  }
-  }
+  if constexpr (STORE_Z)
+    store_tile_logits(acc, region, a, t_base, v_base, wm, wn, lane);
+  else
+    gather_hit_logits(acc, region, a, tt * a.nVt + vt, t_base, wm, wn, lane);
 
   __syncthreads();
   if (t_base + tid < a.rows) {
@@ -506,7 +519,7 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const float2* __restrict__ 
   const int* ir = idx + (r0 + row) * K;
   const float* lr = logp + (r0 + row) * K;
   const float* zr = zhit ? zhit + int64_t(row) * K : nullptr;
-  const float* zrow = z + int64_t(row) * ld_z;
+  const float* zrow = zhit ? nullptr : z + int64_t(row) * ld_z;
   // L_r = Σ_k p_k (logp_k − (z_k − lse)): the log-probability z − lse is
   // formed per entry, so a large common offset of the logits cancels before
   // the sum instead of between two large sums.

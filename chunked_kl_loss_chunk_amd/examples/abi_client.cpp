@@ -3,8 +3,10 @@
 //
 // Reads a problem from a binary file, runs the forward and backward passes of
 // the fused top-K KL loss in float32, and writes the results to a binary file.
+// With a third argument "one-pass" it makes the single kd_fused_kl_fwd_bwd
+// call instead; the output file has the same layout.
 //
-//   abi_client <in.bin> <out.bin>
+//   abi_client <in.bin> <out.bin> [one-pass]
 //
 // in.bin:  int64 N, d, V, K, chunk; then float H[N*d], float W[V*d],
 //          int32 idx[N*K], float logp[N*K], float grad
@@ -16,6 +18,7 @@
 
 #include <cstdint>
 #include <cstdio>
+#include <string>
 #include <vector>
 
 #include "kd_fused_kl.h"
@@ -45,8 +48,9 @@ bool read_all(FILE* f, void* p, size_t n) { return std::fread(p, 1, n, f) == n; 
 }  // namespace
 
 int main(int argc, char** argv) {
-  if (argc != 3) {
-    std::fprintf(stderr, "usage: %s in.bin out.bin\n", argv[0]);
+  const bool one_pass = argc == 4 && std::string(argv[3]) == "one-pass";
+  if (argc != 3 && !one_pass) {
+    std::fprintf(stderr, "usage: %s in.bin out.bin [one-pass]\n", argv[0]);
     return 1;
   }
   FILE* in = std::fopen(argv[1], "rb");
@@ -66,10 +70,13 @@ int main(int argc, char** argv) {
 
   const size_t ws_f = kd_fused_kl_workspace_bytes(KD_PASS_FWD, N, d, V, K, chunk, KD_F32);
   const size_t ws_b = kd_fused_kl_workspace_bytes(KD_PASS_BWD, N, d, V, K, chunk, KD_F32);
-  if (ws_f == 0 || ws_b == 0) {
+  const size_t ws_o = kd_fused_kl_workspace_bytes(KD_PASS_FWD_BWD, N, d, V, K, chunk, KD_F32);
+  if (ws_f == 0 || ws_b == 0 || ws_o == 0) {
     std::fprintf(stderr, "sizes rejected\n");
     return 2;
   }
+  size_t ws_n = ws_f > ws_b ? ws_f : ws_b;
+  if (ws_o > ws_n) ws_n = ws_o;
   void *dH_in, *dW_in, *d_idx, *d_logp, *d_tok, *d_lse, *d_loss, *d_grad, *d_dH, *d_dW, *ws;
   HIP_OK(hipMalloc(&dH_in, H.size() * 4));
   HIP_OK(hipMalloc(&dW_in, W.size() * 4));
@@ -81,7 +88,7 @@ int main(int argc, char** argv) {
   HIP_OK(hipMalloc(&d_grad, 4));
   HIP_OK(hipMalloc(&d_dH, dH.size() * 4 + 4));
   HIP_OK(hipMalloc(&d_dW, dW.size() * 4));
-  HIP_OK(hipMalloc(&ws, ws_f > ws_b ? ws_f : ws_b));
+  HIP_OK(hipMalloc(&ws, ws_n));
   HIP_OK(hipMemcpy(dH_in, H.data(), H.size() * 4, hipMemcpyHostToDevice));
   HIP_OK(hipMemcpy(dW_in, W.data(), W.size() * 4, hipMemcpyHostToDevice));
   HIP_OK(hipMemcpy(d_idx, idx.data(), idx.size() * 4, hipMemcpyHostToDevice));
@@ -90,14 +97,23 @@ int main(int argc, char** argv) {
 
   hipStream_t s;
   HIP_OK(hipStreamCreate(&s));
-  KD_OK_OR_FAIL(kd_fused_kl_fwd(dH_in, dW_in, KD_F32, static_cast<const int32_t*>(d_idx),
-                                static_cast<const float*>(d_logp), N, d, V, K, chunk,
-                                static_cast<float*>(d_tok), static_cast<float*>(d_lse),
-                                static_cast<float*>(d_loss), ws, ws_f, s));
-  KD_OK_OR_FAIL(kd_fused_kl_bwd(dH_in, dW_in, KD_F32, static_cast<const int32_t*>(d_idx),
-                                static_cast<const float*>(d_logp), static_cast<const float*>(d_lse),
-                                N, d, V, K, chunk, static_cast<const float*>(d_grad), d_dH,
-                                static_cast<float*>(d_dW), 0, ws, ws_b, s));
+  if (one_pass) {
+    KD_OK_OR_FAIL(kd_fused_kl_fwd_bwd(
+        dH_in, dW_in, KD_F32, static_cast<const int32_t*>(d_idx), static_cast<const float*>(d_logp),
+        nullptr, KD_REDUCE_SUM, N, d, V, K, chunk, static_cast<const float*>(d_grad),
+        static_cast<float*>(d_tok), static_cast<float*>(d_lse), static_cast<float*>(d_loss), d_dH,
+        static_cast<float*>(d_dW), 0, ws, ws_o, s));
+  } else {
+    KD_OK_OR_FAIL(kd_fused_kl_fwd(dH_in, dW_in, KD_F32, static_cast<const int32_t*>(d_idx),
+                                  static_cast<const float*>(d_logp), N, d, V, K, chunk,
+                                  static_cast<float*>(d_tok), static_cast<float*>(d_lse),
+                                  static_cast<float*>(d_loss), ws, ws_f, s));
+    KD_OK_OR_FAIL(kd_fused_kl_bwd(dH_in, dW_in, KD_F32, static_cast<const int32_t*>(d_idx),
+                                  static_cast<const float*>(d_logp),
+                                  static_cast<const float*>(d_lse), N, d, V, K, chunk,
+                                  static_cast<const float*>(d_grad), d_dH,
+                                  static_cast<float*>(d_dW), 0, ws, ws_b, s));
+  }
   HIP_OK(hipStreamSynchronize(s));
   HIP_OK(hipMemcpy(&loss, d_loss, 4, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(loss_tok.data(), d_tok, N * 4, hipMemcpyDeviceToHost));
@@ -116,7 +132,8 @@ int main(int argc, char** argv) {
   std::fwrite(dH.data(), 4, dH.size(), out);
   std::fwrite(dW.data(), 4, dW.size(), out);
   std::fclose(out);
-  std::printf("abi_client: N=%lld d=%lld V=%lld K=%lld chunk=%lld loss=%.6f\n", (long long)N,
-              (long long)d, (long long)V, (long long)K, (long long)chunk, loss);
+  std::printf("abi_client (%s): N=%lld d=%lld V=%lld K=%lld chunk=%lld loss=%.6f\n",
+              one_pass ? "one-pass" : "two-pass", (long long)N, (long long)d, (long long)V,
+              (long long)K, (long long)chunk, loss);
   return 0;
 }
