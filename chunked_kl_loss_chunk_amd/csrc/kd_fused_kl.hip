@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict_
                                                      uint16_t* __restrict__ dst, int64_t ld_dst,
                                                      int rows_pad) {
   __shared__ uint16_t t[64][66];
-  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64, tid = threadIdx.x;
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64, tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int u = tid + i * 256, rr = u >> 3, cc = (u & 7) * 8;
@@ -554,6 +554,7 @@ __global__ __launch_bounds__(256) void k_fwd_combine(const float2* __restrict__ 
 // same hint on the logit stores slowed the GEMM down more than it saved).
 constexpr int kDlGroups = 8;                             // 4-entry groups per lane
 constexpr int kDlCols = 256 * 4 * kDlGroups;             // entries per workgroup
+static_assert(kDlCols == kStreamCols, "the plan sizes the streaming grid by kStreamCols");
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_dl_dense(const float* __restrict__ z, int64_t ld_z,
                                                   const float* __restrict__ lse,
@@ -1148,42 +1149,46 @@ constexpr int kCheckMaxK = 16384;  // power of two ≥ the largest K of the loss
 // then the row's ids sorted in LDS (bitonic, padded with INT_MAX) and
 // neighbours compared for duplicates. Violations are OR-ed into *flags.
 __global__ __launch_bounds__(256) void k_check_inputs(const int* __restrict__ idx,
-                                                      const float* __restrict__ logp, int K,
-                                                      int V, int* __restrict__ flags) {
+                                                      const float* __restrict__ logp, int64_t N,
+                                                      int K, int V, int* __restrict__ flags) {
   __shared__ int ids[kCheckMaxK];
-  const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   int P = 1;
   while (P < K) P <<= 1;
   int bad = 0;
-  for (int k = tid; k < P; k += 256) {
-    int j = 0x7FFFFFFF;
-    if (k < K) {
-      j = idx[row * K + k];
-      const float lp = logp[row * K + k];
-      if (j < 0 || j >= V) bad |= KD_CHECK_ID_RANGE;
-      if (!(lp <= 0.f)) bad |= KD_CHECK_LOGP;  // positive, +inf or NaN
+  // Rows are taken grid-stride (the grid is capped), one row at a time per
+  // workgroup; the row index is uniform, so every barrier is reached by all.
+  for (int64_t row = blockIdx.x; row < N; row += gridDim.x) {
+    for (int k = tid; k < P; k += 256) {
+      int j = 0x7FFFFFFF;
+      if (k < K) {
+        j = idx[row * K + k];
+        const float lp = logp[row * K + k];
+        if (j < 0 || j >= V) bad |= KD_CHECK_ID_RANGE;
+        if (!(lp <= 0.f)) bad |= KD_CHECK_LOGP;  // positive, +inf or NaN
+      }
+      ids[k] = j;
     }
-    ids[k] = j;
-  }
-  __syncthreads();
-  for (int size = 2; size <= P; size <<= 1)
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < P; i += 256) {
-        const int j = i ^ stride;
-        if (j > i) {
-          const bool up = (i & size) == 0;
-          const int x = ids[i], y = ids[j];
-          if (up ? x > y : x < y) {
-            ids[i] = y;
-            ids[j] = x;
+    __syncthreads();
+    for (int size = 2; size <= P; size <<= 1)
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < P; i += 256) {
+          const int j = i ^ stride;
+          if (j > i) {
+            const bool up = (i & size) == 0;
+            const int x = ids[i], y = ids[j];
+            if (up ? x > y : x < y) {
+              ids[i] = y;
+              ids[j] = x;
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
-    }
-  for (int k = tid + 1; k < K; k += 256)
-    if (ids[k] == ids[k - 1]) bad |= KD_CHECK_DUPLICATE;
+    for (int k = tid + 1; k < K; k += 256)
+      if (ids[k] == ids[k - 1]) bad |= KD_CHECK_DUPLICATE;
+    __syncthreads();  // the next row overwrites ids
+  }
   if (bad) atomicOr(flags, bad);
 }
 
@@ -1264,7 +1269,7 @@ inline int64_t prep_slot(const Plan& p, int64_t r0) { return (r0 / p.C) % p.prep
 ColOp chunk_transposed(const Plan& p, const Ws& ws, const char* Hc, int rows, hipStream_t st) {
   uint16_t* ht = ws.at<uint16_t>(p.off_ht);
   timed(KD_KERNEL_PREP, st, [&] {
-    hipLaunchKernelGGL(k_transpose16, dim3(cdiv(p.d, 64), cdiv(p.C_pad, 64)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_transpose16, dim3(cdiv(p.C_pad, 64), cdiv(p.d, 64)), dim3(256), 0, st,
                        reinterpret_cast<const uint16_t*>(Hc), p.d, rows, int(p.d), ht, p.C_pad,
                        int(p.C_pad));
   });
@@ -1750,8 +1755,8 @@ int kd_fused_kl_check_inputs(const int32_t* topk_idx, const float* topk_logp, in
   hipLaunchKernelGGL(kd::k_fill_i32, dim3(1), dim3(64), 0, s, reinterpret_cast<int*>(flags),
                      int64_t(1), 0);
   if (N > 0)
-    hipLaunchKernelGGL(kd::k_check_inputs, dim3(unsigned(N)), dim3(256), 0, s, topk_idx, topk_logp,
-                       int(K), int(V), reinterpret_cast<int*>(flags));
+    hipLaunchKernelGGL(kd::k_check_inputs, dim3(unsigned(N < 65536 ? N : 65536)), dim3(256), 0, s,
+                       topk_idx, topk_logp, N, int(K), int(V), reinterpret_cast<int*>(flags));
   return kd::launch_status();
 }
 

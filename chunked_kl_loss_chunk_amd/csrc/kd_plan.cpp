@@ -53,10 +53,6 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
   if (q.V_pad * es * kTileM >= (int64_t(1) << 31) || d * es * kTileM >= (int64_t(1) << 31))
     return KD_ERR_UNSUPPORTED;
 
-  // The one-pass streaming kernels run a workgroup per 8192 stored logits:
-  // keep their grids under 2^31 threads.
-  if (pass == KD_PASS_FWD_BWD && q.C * q.V_pad > (int64_t(1) << 36)) return KD_ERR_UNSUPPORTED;
-
   const int64_t n_chunks = N > 0 ? cdiv(N, q.C) : 1;
   int64_t window = kDwRows / q.C;
   if (window > kDwMaxWindow) window = kDwMaxWindow;
@@ -73,6 +69,16 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
   if (splits > q.kt_v) splits = q.kt_v;
   if (splits < 1) splits = 1;
   q.dh_splits = static_cast<int>(splits);
+  // Launch grids, in workgroups of 256 threads: the logit tiles of a chunk
+  // (nb), one workgroup per row (teacher finish), four rows per workgroup
+  // (prep, combine), the dH and dW tiles of a window, and the one-pass
+  // streaming pass over the chunk's stored logits.
+  const int64_t dh_grid = (q.win_rows_pad / kTileM) * cdiv(d, kTileM) * q.dh_splits;
+  const int64_t dw_grid = cdiv(d, kTileM) * q.nVt;
+  const int64_t stream_grid = q.C * cdiv(q.V_pad, kStreamCols);
+  if (q.nb > kMaxBlocks || q.C > kMaxBlocks || dh_grid > kMaxBlocks || dw_grid > kMaxBlocks ||
+      (pass == KD_PASS_FWD_BWD && stream_grid > kMaxBlocks))
+    return KD_ERR_UNSUPPORTED;
   int64_t group = kPrepBuckets / q.nb;
   if (group > kPrepRows / q.C) group = kPrepRows / q.C;
   if (group > n_chunks) group = n_chunks;

@@ -32,6 +32,12 @@ constexpr int64_t kPrepRows = 65536;
 // about kDwRows tokens (at most kDwMaxWindow chunks, at least one).
 constexpr int64_t kDwRows = 4096;
 constexpr int kDwMaxWindow = 4;
+// A launch holds at most 2^32 − 1 work-items per grid dimension: with 256
+// threads per workgroup, at most kMaxBlocks workgroups. The plan rejects
+// sizes whose grids would not fit.
+constexpr int64_t kMaxBlocks = (int64_t(1) << 24) - 1;
+// Stored logits handled by one workgroup of the one-pass streaming kernel.
+constexpr int64_t kStreamCols = 8192;
 
 struct Plan {
   int64_t N, d, V, K, chunk;

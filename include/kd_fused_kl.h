@@ -118,8 +118,11 @@ size_t kd_fused_kl_workspace_bytes(int pass, int64_t N, int64_t d, int64_t V, in
  * N = 0 writes loss_sum = 0. Rows are processed `chunk` at a time.
  *
  * Returns KD_ERR_UNSUPPORTED for sizes the kernels do not take: K > 16383,
- * d > 2^20, N >= 2^31, or a padded vocabulary row of 8 MiB or more
- * (V > 4,194,048 in bf16, V > 2,096,896 in float32).
+ * d > 2^20, N >= 2^31, a padded vocabulary row of 8 MiB or more
+ * (V > 4,194,048 in bf16, V > 2,096,896 in float32), or a chunk so large
+ * that one launch would need 2^24 workgroups or more (the logit tiles of a
+ * chunk, ⌈chunk/256⌉·⌈V/256⌉; the dH or dW tiles of a window; one
+ * workgroup per row of a chunk).
  */
 int kd_fused_kl_fwd(const void* H, const void* W, int dtype, const int32_t* topk_idx,
                     const float* topk_logp, int64_t N, int64_t d, int64_t V, int64_t K,

@@ -288,3 +288,20 @@ def _fb(L, **kw):
 ])
 def test_one_pass_rejects_invalid(L, kw, want):
     assert _fb(L, **kw) == want
+
+
+def test_launch_grid_limit(L):
+    """Every launch holds fewer than 2^24 workgroups of 256 threads (2^32
+    work-items): a chunk whose logit tiles (chunk/256 x V/256) reach 2^24 is
+    rejected, one just below is accepted; the one-pass streaming pass (a
+    workgroup per 8192 stored logits of a row) has its own bound."""
+    ws = L.kd_fused_kl_workspace_bytes
+    bf = _lib.KD_BF16
+    big, below = 1 << 20, (1 << 20) - 256
+    for pass_ in (0, 1, 2):
+        assert ws(pass_, big, 64, big, 8, big, bf) == 0          # 4096 x 4096 tiles
+        assert ws(pass_, big, 64, below, 8, big, bf) > 0         # 4096 x 4095 tiles
+    # the same chunk in the one-pass call: 2^20 rows x 128 workgroups per row
+    assert ws(_lib.KD_PASS_FWD_BWD, big, 64, below, 8, big, bf) == 0
+    assert ws(_lib.KD_PASS_FWD_BWD, 1 << 17, 64, below, 8, 1 << 17, bf) == 0  # 2^17 x 128 = 2^24
+    assert ws(_lib.KD_PASS_FWD_BWD, 1 << 16, 64, below, 8, 1 << 16, bf) > 0
