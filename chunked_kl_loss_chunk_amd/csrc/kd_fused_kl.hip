@@ -28,7 +28,8 @@
 //
 // The offline teacher cache that feeds the loss (top-K ids by logit and their
 // full-softmax log-probabilities; [P1] "As duas mudanças", [P4] 离线蒸馏) is
-// produced by two passes of the same logit GEMM (kd_teacher_topk).
+// produced by one pass of the logit GEMM that keeps the chunk's logits, and a
+// streaming selection over them (kd_teacher_topk).
 //
 // The teacher distribution stays sparse and is not renormalised ([P5] "Čo
 // dopĺňajú podrobnejšie experimenty"). The gradient is the closed form of the
@@ -937,13 +938,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dw(DwArgs a) {
 // offline teacher cache: top-K ids by logit and their full-softmax log-probs
 // --------------------------------------------------------------------------
 // The teacher runs once and keeps the most probable tokens of every position
-// with their log-probabilities, not renormalised. Two passes over the logit
-// GEMM per chunk, no [rows, V] grid:
-//   pass 1  k_fwd_logits with no cached ids: per-tile (max, Σexp) of each row;
+// with their log-probabilities, not renormalised. One pass of the logit GEMM
+// per chunk, whose float32 logits are kept for the chunk only (no [N, V] grid):
+//   logits  k_fwd_logits<…, true>: per-tile (max, Σexp) of each row, and the
+//           chunk's logits stored;
 //   select  lse, and τ = the K-th largest tile maximum: at least K logits of
 //           the row are ≥ τ, so every top-K logit is ≥ τ;
-//   pass 2  the same GEMM (bitwise the same logits): every logit ≥ τ is
-//           appended to its row's candidate list;
+//   scan    every stored logit ≥ τ is appended to its row's candidate list;
 //   finish  an exact radix select of the K-th largest (logit, −id) key among
 //           the row's candidates, then a sort of the K winners.
 
@@ -993,63 +994,53 @@ __global__ __launch_bounds__(256) void k_tk_select(const float2* __restrict__ pa
   }
 }
 
-struct TkArgs {
-  RowOp W;   // teacher head [V][d]
-  RowOp H;   // chunk of teacher hidden states [rows][d] (float32 path)
-  ColOp Ht;  // the same chunk transposed, [d][C_pad] (bf16 path)
-  int kt;
-  int tiles_t, tiles_v;
-  int rows, V;
-  const float* tau;  // [rows]
-  int* cnt;          // [rows] candidates so far
-  uint2* cand;       // [rows][cap]: (float bits of the logit, vocabulary id)
-  int64_t cap;       // ≥ V: a row never overflows
-};
-
-// Pass 2: the logit tile again; every logit at or above its row's τ becomes a
-// candidate. A column block with no candidate in any lane is skipped whole.
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_tk_candidates(TkArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
-  lds_t* smem = (lds_t*)(smem_raw);
-  const int nblk = a.tiles_t * a.tiles_v;
-  const int logical = xcd_logical(blockIdx.x, nblk);
-  const int tt = logical % a.tiles_t, vt = logical / a.tiles_t;
-  const int t_base = tt * kBN, v_base = vt * kBM;
-
-  Acc acc;
-  if constexpr (BF16)
-    gemm_tile<BF16, RowDirect, RowOp, ColDirect, ColOp>(acc, a.W, v_base, a.Ht, t_base, 0, a.kt, smem);
-  else
-    gemm_tile<BF16, RowDirect, RowOp, RowDirect, RowOp>(acc, a.W, v_base, a.H, t_base, 0, a.kt, smem);
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave % kWM, wn = wave / kWM;
-  const int vlim = a.V - (v_base + wm * kWTM);
+// Candidates from the chunk's stored logits ([rows][ld_z] float32): every
+// z_rj ≥ τ_r with j < V joins row r's list as (float bits of z, id). A
+// workgroup scans 8192 logits of one row, as the one-pass dlogits pass does.
+// Each wave counts its lanes' hits, reserves its slots with a single atomic
+// add, and writes them at the lanes' prefix offsets, so the atomic's round
+// trip is paid once per wave, not once per hit. The set is exactly
+// {j : z_rj ≥ τ_r}, in an order that does not matter to the finish.
+__global__ __launch_bounds__(256) void k_tk_scan(const float* __restrict__ z, int64_t ld_z,
+                                                 int nseg, int V, int V_pad,
+                                                 const float* __restrict__ tau,
+                                                 int* __restrict__ cnt, uint2* __restrict__ cand,
+                                                 int64_t cap) {
+  const int row = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+  const int lane = threadIdx.x & 63;
+  const float t = tau[row];
+  const float* zr = z + int64_t(row) * ld_z;
+  const int c0 = seg * kDlCols + threadIdx.x * 4;
+  f32x4_t v[kDlGroups];
 #pragma unroll
-  for (int b = 0; b < kTN; ++b) {
-    const int tok = t_base + acc_col(wn, b, lane);
-    const float tau = tok < a.rows ? a.tau[tok] : __builtin_inff();
-    float m = kNegInf;
-#pragma unroll
-    for (int t = 0; t < kTM; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[t][b][i]);
-    if (__ballot(m >= tau) == 0) continue;
-#pragma unroll
-    for (int t = 0; t < kTM; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = t * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        const float z = acc[t][b][i];
-        if (r < vlim && z >= tau) {
-          const int slot = atomicAdd(a.cnt + tok, 1);
-          a.cand[int64_t(tok) * a.cap + slot] =
-              make_uint2(__float_as_uint(z), uint32_t(v_base + wm * kWTM + r));
-        }
-      }
+  for (int u = 0; u < kDlGroups; ++u) {
+    const int c = c0 + u * 1024;
+    v[u] = f32x4_t{kNegInf, kNegInf, kNegInf, kNegInf};
+    if (c < V_pad) v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(zr + c));
   }
+  const auto hit = [&](int u, int i) { return c0 + u * 1024 + i < V && v[u][i] >= t; };
+  int n = 0;
+#pragma unroll
+  for (int u = 0; u < kDlGroups; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) n += hit(u, i) ? 1 : 0;
+  int incl = n;  // inclusive prefix over the wave's lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  const int total = __shfl(incl, 63);
+  if (total == 0) return;
+  int base = 0;
+  if (lane == 0) base = atomicAdd(cnt + row, total);
+  int pos = __shfl(base, 0) + incl - n;
+  uint2* const cr = cand + int64_t(row) * cap;
+#pragma unroll
+  for (int u = 0; u < kDlGroups; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (hit(u, i)) cr[pos++] = make_uint2(__float_as_uint(v[u][i]), uint32_t(c0 + u * 1024 + i));
 }
 
 constexpr int kTkMaxK = int(kMaxTeacherK);  // the K winners are sorted in LDS
@@ -1534,9 +1525,12 @@ int run_teacher(const Plan& p, const void* Ht, const void* Wt, int32_t* idx, flo
                 float* lse, void* workspace, hipStream_t st) {
   Ws ws{static_cast<char*>(workspace), p};
   if (p.N == 0) return KD_OK;
-  hipLaunchKernelGGL(k_fill_i32, dim3(cdiv(p.nb + 1, 256)), dim3(256), 0, st,
-                     ws.at<int>(p.off_offsets), int64_t(p.nb + 1), 0);
   const int64_t row_bytes = p.d * p.es;
+  float* const z = ws.at<float>(p.off_z);
+  float* const tau = ws.at<float>(p.off_tau);
+  int* const cnt = ws.at<int>(p.off_cnt);
+  uint2* const cand = ws.at<uint2>(p.off_cand);
+  const int nseg = int(cdiv(p.V_pad, kDlCols));
   for (int64_t r0 = 0; r0 < p.N; r0 += p.C) {
     const int rows = int(p.N - r0 < p.C ? p.N - r0 : p.C);
     const char* Hc = static_cast<const char*>(Ht) + r0 * row_bytes;
@@ -1551,40 +1545,27 @@ int run_teacher(const Plan& p, const void* Ht, const void* Wt, int32_t* idx, flo
     a.V = int(p.V);
     a.K = int(p.K);
     a.nVt = int(p.nVt);
-    a.offsets = ws.at<int>(p.off_offsets);
-    a.recs = ws.at<uint2>(p.off_recs);
-    a.zhit = nullptr;  // never written: there are no cached ids
+    a.offsets = nullptr;  // there are no cached ids
+    a.recs = nullptr;
+    a.zhit = nullptr;
     a.part = ws.at<float2>(p.off_part);
-    a.z = nullptr;
-    a.ld_z = 0;
+    a.z = z;
+    a.ld_z = p.V_pad;
     timed(KD_KERNEL_FWD_LOGITS, st, [&] {
-      hipLaunchKernelGGL((k_fwd_logits<BF16, false>), dim3(a.tiles_t * a.tiles_v),
-                         dim3(kThreads), 0, st, a);
+      hipLaunchKernelGGL((k_fwd_logits<BF16, true>), dim3(a.tiles_t * a.tiles_v), dim3(kThreads),
+                         0, st, a);
     });
     float* const lse_c = lse ? lse + r0 : ws.at<float>(p.off_lse);
     timed(KD_KERNEL_OTHER, st, [&] {
       hipLaunchKernelGGL(k_tk_select, dim3(cdiv(rows, 4)), dim3(256), 0, st, a.part, a.nVt, rows,
-                         int(p.K), lse_c, ws.at<float>(p.off_tau), ws.at<int>(p.off_cnt));
+                         int(p.K), lse_c, tau, cnt);
     });
-    TkArgs t;
-    t.W = a.W;
-    t.H = a.H;
-    t.Ht = a.Ht;
-    t.kt = a.kt;
-    t.tiles_t = a.tiles_t;
-    t.tiles_v = a.tiles_v;
-    t.rows = rows;
-    t.V = int(p.V);
-    t.tau = ws.at<float>(p.off_tau);
-    t.cnt = ws.at<int>(p.off_cnt);
-    t.cand = ws.at<uint2>(p.off_cand);
-    t.cap = p.V_pad;
-    timed(KD_KERNEL_FWD_LOGITS, st, [&] {
-      hipLaunchKernelGGL(k_tk_candidates<BF16>, dim3(t.tiles_t * t.tiles_v), dim3(kThreads), 0, st,
-                         t);
+    timed(KD_KERNEL_DL_STREAM, st, [&] {
+      hipLaunchKernelGGL(k_tk_scan, dim3(unsigned(int64_t(rows) * nseg)), dim3(256), 0, st, z,
+                         p.V_pad, nseg, int(p.V), int(p.V_pad), tau, cnt, cand, p.V_pad);
     });
     timed(KD_KERNEL_OTHER, st, [&] {
-      hipLaunchKernelGGL(k_tk_finish, dim3(rows), dim3(256), 0, st, t.cand, t.cap, t.cnt, lse_c,
+      hipLaunchKernelGGL(k_tk_finish, dim3(rows), dim3(256), 0, st, cand, p.V_pad, cnt, lse_c,
                          int(p.K), idx + r0 * p.K, logp + r0 * p.K);
     });
   }

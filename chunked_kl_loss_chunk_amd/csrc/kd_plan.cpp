@@ -71,13 +71,13 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
   q.dh_splits = static_cast<int>(splits);
   // Launch grids, in workgroups of 256 threads: the logit tiles of a chunk
   // (nb), one workgroup per row (teacher finish), four rows per workgroup
-  // (prep, combine), the dH and dW tiles of a window, and the one-pass
-  // streaming pass over the chunk's stored logits.
+  // (prep, combine), the dH and dW tiles of a window, and the streaming
+  // passes over a chunk's stored logits (one-pass loss, teacher cache).
   const int64_t dh_grid = (q.win_rows_pad / kTileM) * cdiv(d, kTileM) * q.dh_splits;
   const int64_t dw_grid = cdiv(d, kTileM) * q.nVt;
   const int64_t stream_grid = q.C * cdiv(q.V_pad, kStreamCols);
   if (q.nb > kMaxBlocks || q.C > kMaxBlocks || dh_grid > kMaxBlocks || dw_grid > kMaxBlocks ||
-      (pass == KD_PASS_FWD_BWD && stream_grid > kMaxBlocks))
+      ((pass == KD_PASS_FWD_BWD || pass == KD_PASS_TEACHER) && stream_grid > kMaxBlocks))
     return KD_ERR_UNSUPPORTED;
   int64_t group = kPrepBuckets / q.nb;
   if (group > kPrepRows / q.C) group = kPrepRows / q.C;
@@ -92,12 +92,13 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
     return o;
   };
   q.off_flag = take(256);
-  if (pass == KD_PASS_FWD_BWD) {
+  if (pass == KD_PASS_FWD_BWD || pass == KD_PASS_TEACHER) {
     // No buckets: the logits of a chunk are stored, so the cached entries are
-    // read per row. S_r of one chunk.
+    // read per row (one-pass loss: S_r of one chunk), or there are none
+    // (teacher cache).
     q.prep_chunks = 1;
     q.off_counts = q.off_offsets = q.off_recs = 0;
-    q.off_rowS = take(sizeof(float) * size_t(q.C));
+    q.off_rowS = pass == KD_PASS_FWD_BWD ? take(sizeof(float) * size_t(q.C)) : 0;
   } else {
     // Prep buffers of one group of chunks: bucket counts and offsets (chunk
     // slot major), hit records, S_r.
@@ -109,8 +110,9 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
   q.off_ht = dtype == KD_BF16 ? take(size_t(es) * size_t(d) * size_t(q.C_pad)) : 0;
   q.off_z = 0;
   if (pass == KD_PASS_TEACHER) {
-    // No cached ids: the bucket offsets stay zero, so the logit kernel sees
-    // empty hit lists. Candidates: up to V_pad per row, so none overflows.
+    // The chunk's logits (float32, [C][V_pad]), tile partials, lse, τ, and
+    // candidate lists of up to V_pad entries per row, so none overflows.
+    q.off_z = take(sizeof(float) * size_t(q.C) * size_t(q.V_pad));
     q.off_part = take(8 * size_t(q.C_pad * q.nVt));
     q.off_lse = take(sizeof(float) * size_t(q.C_pad));
     q.off_tau = take(sizeof(float) * size_t(q.C_pad));

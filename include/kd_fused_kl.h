@@ -237,12 +237,14 @@ int kd_fused_kl_fwd_bwd(const void* H, const void* W, int dtype, const int32_t* 
  *  topk_logp  [N, K] float32 out — z_r,idx − lse_r.
  *  lse        [N] float32 out, or NULL — log Σ_j exp z_rj of every row.
  *
- * Rows are processed `chunk` at a time with two passes of the logit GEMM and
- * no [N, V] grid: the workspace (kd_fused_kl_workspace_bytes with
- * KD_PASS_TEACHER) holds per-row candidate lists of up to V entries of 8
- * bytes, so it is about chunk × V × 8 bytes. The selection is exact on the
- * float32 logits the kernels compute. Errors as for kd_fused_kl_fwd; K > 2048
- * is KD_ERR_UNSUPPORTED.
+ * Rows are processed `chunk` at a time with one pass of the logit GEMM and
+ * no [N, V] grid: the chunk's float32 logits are kept until its candidates
+ * (logits at or above a per-row threshold that bounds the K-th largest) are
+ * collected. The workspace (kd_fused_kl_workspace_bytes with
+ * KD_PASS_TEACHER) holds those logits and per-row candidate lists of up to V
+ * entries of 8 bytes, so it is about chunk × V × 12 bytes. The selection is
+ * exact on the float32 logits the kernels compute. Errors as for
+ * kd_fused_kl_fwd; K > 2048 is KD_ERR_UNSUPPORTED.
  */
 int kd_teacher_topk(const void* Ht, const void* Wt, int dtype, int64_t N, int64_t d, int64_t V,
                     int64_t K, int64_t chunk, int32_t* topk_idx, float* topk_logp, float* lse,
@@ -284,9 +286,10 @@ int kd_cast_f32_to_bf16(const float* src, void* dst, int64_t n, void* stream);
  * (total_ms[KD_KERNEL_CLASSES]) and launch counts
  * (launches[KD_KERNEL_CLASSES]), and clears the record. A "launch" of
  * KD_KERNEL_PREP is the three prep kernels of one group of chunks, or the
- * transpose of one chunk of H. The teacher cache's two GEMM passes count as
- * KD_KERNEL_FWD_LOGITS, and so does the logit pass of kd_fused_kl_fwd_bwd,
- * which also stores the logits. Global state, not thread-safe; this is the one entry
+ * transpose of one chunk of H. The logit pass of the teacher cache and of
+ * kd_fused_kl_fwd_bwd, which also store the logits, count as
+ * KD_KERNEL_FWD_LOGITS; their streaming passes over the stored logits as
+ * KD_KERNEL_DL_STREAM. Global state, not thread-safe; this is the one entry
  * point that synchronises (with its own events).
  */
 enum {
@@ -296,7 +299,7 @@ enum {
   KD_KERNEL_BWD_DH = 3,       /* dH = dlogits W                               */
   KD_KERNEL_BWD_DW = 4,       /* dW (+)= dlogitsᵀ H                           */
   KD_KERNEL_OTHER = 5,        /* combine, split reduce, teacher select/finish */
-  KD_KERNEL_DL_STREAM = 6,    /* kd_fused_kl_fwd_bwd: stored logits -> dlogits */
+  KD_KERNEL_DL_STREAM = 6,    /* stored logits -> dlogits, or teacher candidates */
   KD_KERNEL_CLASSES = 7
 };
 int kd_timing_enable(int enable);

@@ -255,10 +255,13 @@ def test_one_pass_workspace(L):
     # the extra over the backward is the chunk's logits (and small per-chunk buffers)
     wb = ws(b, 8192, 3072, 128256, 100, 1024, bf)
     assert 1024 * V_pad * 4 - (8 * 100 * 8192 + (1 << 22)) < w1 - wb <= 1024 * V_pad * 4 + (1 << 23)
-    # the streaming kernels' grid bound: chunk x V_pad <= 2^36
-    assert ws(o, 1 << 20, 64, 1 << 16, 8, 1 << 20, _lib.KD_F32) > 0
-    assert ws(o, 1 << 21, 64, 1 << 16, 8, 1 << 21, _lib.KD_F32) == 0
-    for pass_ in (0, 1, 2):
+    # the streaming pass over the stored logits (one-pass loss and teacher
+    # cache) takes a workgroup per 8192 logits of a row: chunk x V_pad / 8192
+    # workgroups must stay below 2^24
+    for pass_ in (o, _lib.KD_PASS_TEACHER):
+        assert ws(pass_, 1 << 20, 64, 1 << 16, 8, 1 << 20, _lib.KD_F32) > 0
+        assert ws(pass_, 1 << 21, 64, 1 << 16, 8, 1 << 21, _lib.KD_F32) == 0
+    for pass_ in (0, 1):
         assert ws(pass_, 1 << 21, 64, 1 << 16, 8, 1 << 21, _lib.KD_F32) > 0
 
 
@@ -298,10 +301,13 @@ def test_launch_grid_limit(L):
     ws = L.kd_fused_kl_workspace_bytes
     bf = _lib.KD_BF16
     big, below = 1 << 20, (1 << 20) - 256
-    for pass_ in (0, 1, 2):
+    for pass_ in (0, 1, 2, 3):
         assert ws(pass_, big, 64, big, 8, big, bf) == 0          # 4096 x 4096 tiles
+    for pass_ in (0, 1):
         assert ws(pass_, big, 64, below, 8, big, bf) > 0         # 4096 x 4095 tiles
-    # the same chunk in the one-pass call: 2^20 rows x 128 workgroups per row
+    # the same chunk with a streaming pass over its stored logits (teacher
+    # cache, one-pass call): 2^20 rows x 128 workgroups per row
+    assert ws(_lib.KD_PASS_TEACHER, big, 64, below, 8, big, bf) == 0
     assert ws(_lib.KD_PASS_FWD_BWD, big, 64, below, 8, big, bf) == 0
     assert ws(_lib.KD_PASS_FWD_BWD, 1 << 17, 64, below, 8, 1 << 17, bf) == 0  # 2^17 x 128 = 2^24
     assert ws(_lib.KD_PASS_FWD_BWD, 1 << 16, 64, below, 8, 1 << 16, bf) > 0

@@ -95,6 +95,21 @@ def test_teacher_topk_integer_logits_exact_with_ties(kd, dtype):
     np.testing.assert_allclose(logp, ref["logp"], rtol=0, atol=TOL_LOGP)
 
 
+@pytest.mark.parametrize("V,chunk", [(20000, 128), (8192, 300)])
+def test_teacher_topk_uniform_teacher(kd, V, chunk):
+    # A zero head: every logit of every row is 0, so τ = 0 and all V logits
+    # are candidates (the lists fill to V entries; V = 20,000 spans three
+    # 8192-logit scan workgroups per row, the last one ragged). The kept ids
+    # are the K lowest, each with log-probability −ln V.
+    N, d, K = 300, 64, 64
+    Ht = torch.randn(N, d, generator=torch.Generator().manual_seed(65))
+    Wt = torch.zeros(V, d)
+    idx, logp, lse = _run(kd, Ht, Wt, K, chunk)
+    assert np.array_equal(idx, np.tile(np.arange(K, dtype=idx.dtype), (N, 1)))
+    np.testing.assert_allclose(logp, -math.log(V), rtol=0, atol=TOL_LOGP)
+    np.testing.assert_allclose(lse, math.log(V), rtol=1e-6, atol=0)
+
+
 def test_teacher_cache_feeds_the_loss(kd):
     # The producer's cache, used as the loss's teacher input, gives the loss
     # the oracle's cache gives (end to end through both entry points).
