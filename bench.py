@@ -111,15 +111,35 @@ def run_gpu(cfg, steps, warmup, dev):
     resident = torch.cuda.memory_allocated(dev)
     L.kd_timing_enable(1)
     _kernel_stats(L)  # clear
+    # Events on the stream the library launches on (torch's current stream)
+    # between steps give per-step times for the median; the wall clock around
+    # all steps gives the reported mean.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    ev[0].record()
+    for i in range(steps):
         step()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kstats = _kernel_stats(L)
     L.kd_timing_enable(0)
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    median_ms = per_step[steps // 2] if steps % 2 else 0.5 * (per_step[steps // 2 - 1] + per_step[steps // 2])
     peak = torch.cuda.max_memory_allocated(dev)
+    # The forward and the backward pass, each timed alone.
+    _, _, lse = kd.kl_forward(H, W, idx, logp, cfg.chunk, want_loss_tok=False)
+    torch.cuda.synchronize()
+    f0 = time.perf_counter()
+    for _ in range(steps):
+        kd.kl_forward(H, W, idx, logp, cfg.chunk, want_loss_tok=False)
+    torch.cuda.synchronize()
+    f1 = time.perf_counter()
+    for _ in range(steps):
+        kd.kl_backward(H, W, idx, logp, lse, g, cfg.chunk, dW_out=dW, accumulate=False)
+    torch.cuda.synchronize()
+    b1 = time.perf_counter()
     # The same step captured once into a HIP graph and replayed: no host
     # launch gaps between the ~60 kernels of a step.
     graph_s = None
@@ -146,6 +166,9 @@ def run_gpu(cfg, steps, warmup, dev):
     one = _time_one_pass(kd, L, H, W, idx, logp, g, dW, cfg.chunk, steps, warmup, dev)
     return {
         "sec_per_step": (t1 - t0) / steps,
+        "median_ms_per_step": median_ms,
+        "fwd_sec_per_step": (f1 - f0) / steps,
+        "bwd_sec_per_step": (b1 - f1) / steps,
         "graph_sec_per_step": graph_s,
         "kernels": kstats,
         "peak_hbm_bytes": int(peak),
@@ -185,6 +208,21 @@ def _time_one_pass(kd, L, H, W, idx, logp, g, dW, chunk, steps, warmup, dev):
             "peak_hbm_bytes": int(torch.cuda.max_memory_allocated(dev))}
 
 
+def _host_info():
+    """The host the oracle runs on: CPU model, logical CPUs, CPUs this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpu_count": os.cpu_count(),
+            "cpus_available": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(cfg, H, W, idx, logp, rows):
     """The CPU oracle as it stands, on the first `rows` rows of the workload."""
     import numpy as np  # noqa: F401
@@ -211,6 +249,9 @@ def cpu_baseline(cfg, H, W, idx, logp, rows):
         "kind": "oracle",
         "sample": (f"first {rows} of {cfg.N} rows of the workload (d={cfg.d}, V={cfg.V}, "
                    f"K={cfg.K}), dense fp64 forward+backward incl. dW; {dt:.1f} s"),
+        # the dense oracle's three contractions: Z = H Wᵀ, dH = G W, dW = Gᵀ H
+        "gflops": 6.0 * rows * cfg.d * cfg.V / dt / 1e9,
+        **_host_info(),
     }
 
 
@@ -396,6 +437,9 @@ def main():
         "peak_hbm_bytes": r["peak_hbm_bytes"],
         "resident_input_bytes": r["resident_bytes"],
         "kernels": kernels_out,
+        "median_ms_per_step": r["median_ms_per_step"],
+        "fwd_ms_per_step": r["fwd_sec_per_step"] * 1e3,
+        "bwd_ms_per_step": r["bwd_sec_per_step"] * 1e3,
         "graph_ms_per_step": None if r["graph_sec_per_step"] is None else r["graph_sec_per_step"] * 1e3,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": _traffic(dom, cfg.name)},
