@@ -57,12 +57,10 @@ struct Elt;
 template <>
 struct Elt<true> {
   typedef __bf16 T;
-  static constexpr int size = 2;
 };
 template <>
 struct Elt<false> {
   typedef float T;
-  static constexpr int size = 4;
 };
 
 // Hit record of one cached teacher entry inside a logit tile.

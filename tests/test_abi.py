@@ -311,3 +311,53 @@ def test_launch_grid_limit(L):
     assert ws(_lib.KD_PASS_FWD_BWD, big, 64, below, 8, big, bf) == 0
     assert ws(_lib.KD_PASS_FWD_BWD, 1 << 17, 64, below, 8, 1 << 17, bf) == 0  # 2^17 x 128 = 2^24
     assert ws(_lib.KD_PASS_FWD_BWD, 1 << 16, 64, below, 8, 1 << 16, bf) > 0
+
+
+C_CLIENT = r"""
+#include <stdio.h>
+#include "kd_fused_kl.h"
+
+int main(void) {
+  /* every entry point the header declares, taken by address from C */
+  typedef void (*fn_t)(void);
+  const fn_t fns[] = {
+      (fn_t)kd_status_str, (fn_t)kd_fused_kl_workspace_bytes,
+      (fn_t)kd_fused_kl_fwd, (fn_t)kd_fused_kl_bwd,
+      (fn_t)kd_fused_kl_fwd_ex, (fn_t)kd_fused_kl_bwd_ex,
+      (fn_t)kd_fused_kl_fwd_bwd, (fn_t)kd_teacher_topk,
+      (fn_t)kd_fused_kl_check_inputs, (fn_t)kd_cast_f32_to_bf16,
+      (fn_t)kd_timing_enable, (fn_t)kd_timing_read};
+  for (unsigned i = 0; i < sizeof(fns) / sizeof(fns[0]); ++i)
+    if (!fns[i]) return 3;
+  size_t ws = kd_fused_kl_workspace_bytes(KD_PASS_FWD_BWD, 8192, 3072, 128256, 100, 1024, KD_BF16);
+  int st = kd_fused_kl_fwd(0, 0, KD_F32, 0, 0, -1, 64, 1000, 8, 32, 0, 0, 0, 0, 0, 0);
+  printf("%zu %s %d\n", ws, kd_status_str(st), KD_KERNEL_CLASSES);
+  return ws > 0 && st == KD_ERR_INVALID_ARG ? 0 : 4;
+}
+"""
+
+
+def test_header_is_plain_c(tmp_path):
+    """The header compiles as C99 (gcc, no C++), and a C program linked
+    against the library calls its host-only entry points."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    if not os.path.exists(_build.LIB_PATH):
+        _build.build()
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    libdir = os.path.dirname(_build.LIB_PATH)
+    cmd = [gcc, "-std=c99", "-Wall", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+           str(src), "-o", str(exe), "-L", libdir, "-lkdkl", f"-Wl,-rpath,{libdir}"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, (run.stdout, run.stderr)
+    ws, status, classes = run.stdout.split()
+    assert int(ws) == _lib.lib().kd_fused_kl_workspace_bytes(3, 8192, 3072, 128256, 100, 1024, 1)
+    assert status == "KD_ERR_INVALID_ARG" and int(classes) == len(_lib.KERNEL_CLASSES)
