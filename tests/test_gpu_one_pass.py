@@ -223,3 +223,12 @@ def test_full_size_gpt_oss_head(kd):
     cfg = workload.config(5)
     _full_size(kd, cfg, [0, 2047, 2048, 16383, cfg.N - 1])
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_full_size_long_context_262k(kd):
+    # The longest point of the long-context sweep: 262,144 tokens in 2,048-row
+    # chunks, 64 dW windows of two chunks each.
+    cfg = workload.config(4, N=workload.SWEEP_N[-1])
+    _full_size(kd, cfg, [0, 2047, 2048, 4095, 4096, cfg.N // 2, cfg.N - 1])
+    torch.cuda.empty_cache()

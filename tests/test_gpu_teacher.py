@@ -146,6 +146,18 @@ def test_teacher_topk_full_size_sampled_rows(kd):
     check_rows(idx[rows], logp[rows], lse[rows], ref, K)
 
 
+def test_teacher_topk_gpt_oss_vocabulary_sampled_rows(kd):
+    # The gpt-oss vocabulary (V = 201,088: a ragged last tile and 25 streaming
+    # workgroups per row) with d = 2880, over 2,500 positions in 1,024-row
+    # chunks; 10 sampled rows against the oracle.
+    N, d, V, K = 2500, 2880, 201088, 100
+    Ht, Wt = _inputs(N, d, V, "bf16", seed=66)
+    idx, logp, lse = _run(kd, Ht, Wt, K, 1024)
+    rows = np.array([0, 1, 1023, 1024, 1500, 2047, 2048, 2400, 2498, 2499])
+    ref = oracle.teacher_topk_reference(Ht[rows].double().numpy(), Wt.double().numpy(), K)
+    check_rows(idx[rows], logp[rows], lse[rows], ref, K)
+
+
 def test_teacher_topk_bitwise_repeatable(kd):
     Ht, Wt = _inputs(400, 96, 9000, "bf16", seed=64)
     a = _run(kd, Ht, Wt, 64, 128)
