@@ -957,11 +957,10 @@ __device__ __forceinline__ float fkey_inv(uint32_t k) {
 
 // One wave per row: lse_r from the tile partials (fixed order) and τ_r, the
 // K-th largest tile maximum (bit-by-bit search of its key), or −inf when the
-// vocabulary has fewer than K tiles. Resets the row's candidate count.
+// vocabulary has fewer than K tiles.
 __global__ __launch_bounds__(256) void k_tk_select(const float2* __restrict__ part, int nVt,
                                                    int rows, int K, float* __restrict__ lse_out,
-                                                   float* __restrict__ tau_out,
-                                                   int* __restrict__ cnt) {
+                                                   float* __restrict__ tau_out) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
   const float2* pr = part + int64_t(row) * nVt;
@@ -988,24 +987,25 @@ __global__ __launch_bounds__(256) void k_tk_select(const float2* __restrict__ pa
   if (lane == 0) {
     lse_out[row] = m + __logf(s);
     tau_out[row] = tau;
-    cnt[row] = 0;
   }
 }
 
 // Candidates from the chunk's stored logits ([rows][ld_z] float32): every
 // z_rj ≥ τ_r with j < V joins row r's list as (float bits of z, id). A
-// workgroup scans 8192 logits of one row, as the one-pass dlogits pass does.
-// Each wave counts its lanes' hits, reserves its slots with a single atomic
-// add, and writes them at the lanes' prefix offsets, so the atomic's round
-// trip is paid once per wave, not once per hit. The set is exactly
-// {j : z_rj ≥ τ_r}, in an order that does not matter to the finish.
+// workgroup scans 8192 logits of one row (segment seg), as the one-pass
+// dlogits pass does, and owns the list slots [seg·8192, seg·8192 + its
+// count): a segment never holds more candidates than logits, so no slot is
+// shared and no atomic is needed. The waves' hit counts are combined by a
+// prefix sum over lanes and then over the four waves; the count goes to
+// cnt[row·nseg + seg]. The set is exactly {j : z_rj ≥ τ_r}.
 __global__ __launch_bounds__(256) void k_tk_scan(const float* __restrict__ z, int64_t ld_z,
                                                  int nseg, int V, int V_pad,
                                                  const float* __restrict__ tau,
                                                  int* __restrict__ cnt, uint2* __restrict__ cand,
                                                  int64_t cap) {
+  __shared__ int wave_total[4];
   const int row = blockIdx.x / nseg, seg = blockIdx.x % nseg;
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float t = tau[row];
   const float* zr = z + int64_t(row) * ld_z;
   const int c0 = seg * kDlCols + threadIdx.x * 4;
@@ -1028,12 +1028,17 @@ __global__ __launch_bounds__(256) void k_tk_scan(const float* __restrict__ z, in
     const int y = __shfl_up(incl, off);
     if (lane >= off) incl += y;
   }
-  const int total = __shfl(incl, 63);
-  if (total == 0) return;
-  int base = 0;
-  if (lane == 0) base = atomicAdd(cnt + row, total);
-  int pos = __shfl(base, 0) + incl - n;
-  uint2* const cr = cand + int64_t(row) * cap;
+  if (lane == 63) wave_total[wave] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    base += w < wave ? wave_total[w] : 0;
+    total += wave_total[w];
+  }
+  if (threadIdx.x == 0) cnt[int64_t(row) * nseg + seg] = total;
+  uint2* const cr = cand + int64_t(row) * cap + int64_t(seg) * kDlCols;
+  int pos = base + incl - n;
 #pragma unroll
   for (int u = 0; u < kDlGroups; ++u)
 #pragma unroll
@@ -1051,24 +1056,44 @@ __device__ __forceinline__ uint64_t tk_key(uint2 c) {
 // One workgroup per row: the K-th largest key by an 8-bit radix select over
 // the row's candidates, the K keys at or above it gathered (keys are unique,
 // so exactly K), sorted by a bitonic network, and written out with
-// logp = z − lse.
+// logp = z − lse. The candidates sit in nseg segments of 8192 slots
+// (k_tk_scan); candidate i of the row is found through the segments' prefix
+// sums, kept in LDS.
+constexpr int kTkMaxSegs = int(kMaxTeacherSegs);  // the plan rejects larger vocabularies
 __global__ __launch_bounds__(256) void k_tk_finish(const uint2* __restrict__ cand, int64_t cap,
-                                                   const int* __restrict__ cnt,
+                                                   const int* __restrict__ cnt, int nseg,
                                                    const float* __restrict__ lse, int K,
                                                    int32_t* __restrict__ idx_out,
                                                    float* __restrict__ logp_out) {
   __shared__ uint32_t hist[256];
   __shared__ uint64_t keys[kTkMaxK];
+  __shared__ int seg_start[kTkMaxSegs + 1];
   __shared__ uint64_t s_prefix;
   __shared__ int s_krem, s_sel;
   const int row = blockIdx.x, tid = threadIdx.x;
-  const int n = cnt[row];
   const uint2* list = cand + int64_t(row) * cap;
+  for (int sg = tid; sg < nseg; sg += 256) seg_start[sg + 1] = cnt[int64_t(row) * nseg + sg];
   if (tid == 0) {
     s_prefix = 0;
     s_krem = K;
     s_sel = 0;
   }
+  __syncthreads();
+  if (tid == 0) {
+    seg_start[0] = 0;
+    for (int sg = 0; sg < nseg; ++sg) seg_start[sg + 1] += seg_start[sg];
+  }
+  __syncthreads();
+  const int n = seg_start[nseg];
+  // Candidate i: the last segment starting at or before i holds it.
+  const auto at = [&](int i) {
+    int lo = 0, hi = nseg;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (seg_start[mid] <= i) lo = mid; else hi = mid;
+    }
+    return list[int64_t(lo) * kDlCols + (i - seg_start[lo])];
+  };
   uint64_t mask = 0;
   for (int pass = 7; pass >= 0; --pass) {
     hist[tid] = 0u;
@@ -1076,7 +1101,7 @@ __global__ __launch_bounds__(256) void k_tk_finish(const uint2* __restrict__ can
     const uint64_t prefix = s_prefix;
     const int shift = 8 * pass;
     for (int i = tid; i < n; i += 256) {
-      const uint64_t key = tk_key(list[i]);
+      const uint64_t key = tk_key(at(i));
       if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
@@ -1094,7 +1119,7 @@ __global__ __launch_bounds__(256) void k_tk_finish(const uint2* __restrict__ can
   }
   const uint64_t kth = s_prefix;
   for (int i = tid; i < n; i += 256) {
-    const uint64_t key = tk_key(list[i]);
+    const uint64_t key = tk_key(at(i));
     if (key >= kth) {
       const int slot = atomicAdd(&s_sel, 1);
       if (slot < kTkMaxK) keys[slot] = key;
@@ -1556,15 +1581,15 @@ int run_teacher(const Plan& p, const void* Ht, const void* Wt, int32_t* idx, flo
     float* const lse_c = lse ? lse + r0 : ws.at<float>(p.off_lse);
     timed(KD_KERNEL_OTHER, st, [&] {
       hipLaunchKernelGGL(k_tk_select, dim3(cdiv(rows, 4)), dim3(256), 0, st, a.part, a.nVt, rows,
-                         int(p.K), lse_c, tau, cnt);
+                         int(p.K), lse_c, tau);
     });
     timed(KD_KERNEL_DL_STREAM, st, [&] {
       hipLaunchKernelGGL(k_tk_scan, dim3(unsigned(int64_t(rows) * nseg)), dim3(256), 0, st, z,
                          p.V_pad, nseg, int(p.V), int(p.V_pad), tau, cnt, cand, p.V_pad);
     });
     timed(KD_KERNEL_OTHER, st, [&] {
-      hipLaunchKernelGGL(k_tk_finish, dim3(rows), dim3(256), 0, st, cand, p.V_pad, cnt, lse_c,
-                         int(p.K), idx + r0 * p.K, logp + r0 * p.K);
+      hipLaunchKernelGGL(k_tk_finish, dim3(rows), dim3(256), 0, st, cand, p.V_pad, cnt, nseg,
+                         lse_c, int(p.K), idx + r0 * p.K, logp + r0 * p.K);
     });
   }
   return launch_status();

@@ -25,6 +25,8 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
   if ((d * es) % 16 != 0) return KD_ERR_INVALID_ARG;
   if (K > kMaxK) return KD_ERR_UNSUPPORTED;
   if (pass == KD_PASS_TEACHER && K > kMaxTeacherK) return KD_ERR_UNSUPPORTED;
+  if (pass == KD_PASS_TEACHER && cdiv(cdiv(V, kTileN) * kTileN, kStreamCols) > kMaxTeacherSegs)
+    return KD_ERR_UNSUPPORTED;
   // 32-bit limits inside the kernels (row counts, tile counts, per-chunk
   // entry counts); global byte offsets are computed in 64 bits.
   if (N > (int64_t(1) << 31) - 1 || V > (int64_t(1) << 28) || d > (int64_t(1) << 20))
@@ -116,7 +118,8 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
     q.off_part = take(8 * size_t(q.C_pad * q.nVt));
     q.off_lse = take(sizeof(float) * size_t(q.C_pad));
     q.off_tau = take(sizeof(float) * size_t(q.C_pad));
-    q.off_cnt = take(sizeof(int32_t) * size_t(q.C_pad));
+    // candidate counts per row and 8192-logit scan segment
+    q.off_cnt = take(sizeof(int32_t) * size_t(q.C_pad) * size_t(cdiv(q.V_pad, kStreamCols)));
     q.off_cand = take(8 * size_t(q.C_pad) * size_t(q.V_pad));
   } else if (pass == KD_PASS_FWD) {
     q.off_zhit = take(sizeof(float) * size_t(q.C * K));

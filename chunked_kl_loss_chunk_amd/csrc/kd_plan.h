@@ -36,8 +36,11 @@ constexpr int kDwMaxWindow = 4;
 // threads per workgroup, at most kMaxBlocks workgroups. The plan rejects
 // sizes whose grids would not fit.
 constexpr int64_t kMaxBlocks = (int64_t(1) << 24) - 1;
-// Stored logits handled by one workgroup of the one-pass streaming kernel.
+// Stored logits handled by one workgroup of the streaming kernels (one-pass
+// dlogits, teacher candidate scan).
 constexpr int64_t kStreamCols = 8192;
+// Scan segments of one row the teacher cache's finish kernel indexes in LDS.
+constexpr int64_t kMaxTeacherSegs = 512;
 
 struct Plan {
   int64_t N, d, V, K, chunk;
