@@ -35,6 +35,7 @@ SIGNATURES = {
                              _vp]),
     "kd_fused_kl_check_inputs": (_i, [_vp, _vp, _i64, _i64, _i64, _vp, _vp]),
     "kd_cast_f32_to_bf16": (_i, [_vp, _vp, _i64, _vp]),
+    "kd_scale": (_i, [_vp, _i, _i64, _vp, _vp]),
     "kd_timing_enable": (_i, [_i]),
     "kd_timing_read": (_i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
 }

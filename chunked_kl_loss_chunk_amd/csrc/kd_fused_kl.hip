@@ -100,6 +100,19 @@ __global__ void k_fill_f32(float* __restrict__ p, int64_t n, float v) {
     p[i] = v;
 }
 
+// x *= s in place (s a device scalar). Every workgroup reads s first and
+// leaves at once when s == 1, so scaling by one costs only the launch.
+template <bool BF16>
+__global__ void k_scale(void* __restrict__ x, int64_t n, const float* __restrict__ s) {
+  const float g = *s;
+  if (g == 1.f) return;
+  typedef typename Elt<BF16>::T T;
+  T* const p = static_cast<T*>(x);
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = T(float(p[i]) * g);
+}
+
 __global__ void k_cast_f32_bf16(const float* __restrict__ src, __bf16* __restrict__ dst, int64_t n) {
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
        i += int64_t(gridDim.x) * blockDim.x)
@@ -1789,6 +1802,19 @@ int kd_timing_read(double* total_ms, int64_t* launches) {
   kd::g_timing_recs.clear();
   kd::g_events_used = 0;
   return st;
+}
+
+int kd_scale(void* x, int dtype, int64_t n, const float* s, void* stream) {
+  if (n < 0 || (dtype != KD_F32 && dtype != KD_BF16)) return KD_ERR_INVALID_ARG;
+  if (n == 0) return KD_OK;
+  if (!x || !s || !kd::aligned(x, dtype == KD_BF16 ? 2 : 4) || !kd::aligned(s, 4))
+    return KD_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == KD_BF16)
+    hipLaunchKernelGGL(kd::k_scale<true>, dim3(4096), dim3(256), 0, st, x, n, s);
+  else
+    hipLaunchKernelGGL(kd::k_scale<false>, dim3(4096), dim3(256), 0, st, x, n, s);
+  return kd::launch_status();
 }
 
 int kd_cast_f32_to_bf16(const float* src, void* dst, int64_t n, void* stream) {

@@ -251,16 +251,42 @@ def cast_f32_to_bf16(x: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def scale_(x: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
+    """x *= s in place on the GPU (x fp32 or bf16, s a 1-element fp32 device
+    tensor); nothing but a launch when s == 1."""
+    if not (x.is_cuda and x.is_contiguous()):
+        raise ValueError("expected a contiguous GPU tensor")
+    s = s.reshape(1).to(device=x.device, dtype=torch.float32).contiguous()
+    st = _lib.lib().kd_scale(_p(x), dtype_code(x.dtype), x.numel(), _p(s), _stream(x.device))
+    _lib.check("kd_scale", st)
+    return x
+
+
 class FusedTopKKL(torch.autograd.Function):
     """Σ over positions of w_r · KL(teacher top-K ‖ student softmax(H Wᵀ)), or
     its weighted mean.
 
-    Saves only lse [N] between the passes; the backward pass recomputes the
-    logits chunk by chunk.
+    Two-pass (default): saves only lse [N] between the passes; the backward
+    pass recomputes the logits chunk by chunk. One-pass: the forward computes
+    the loss and the gradients at an upstream gradient of 1 in one call
+    (each chunk projected once) and keeps dH and dW; the backward scales them
+    by the upstream gradient (a no-op launch when it is 1). A second backward
+    through the same graph is then refused, since the kept gradients were
+    scaled in place by the first.
     """
 
     @staticmethod
-    def forward(ctx, H, W, idx, logp, chunk, weight, reduction):
+    def forward(ctx, H, W, idx, logp, chunk, weight, reduction, one_pass):
+        need_dH, need_dW = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        ctx.one_pass = bool(one_pass) and (need_dH or need_dW)
+        if ctx.one_pass:
+            loss, _, _, dH, dW = kl_forward_backward(
+                H, W, idx, logp, chunk, want_loss_tok=False, need_dH=need_dH, need_dW=need_dW,
+                weight=weight, reduction=reduction)
+            ctx.save_for_backward(dH, dW)
+            ctx.w_dtype = W.dtype
+            ctx.spent = False
+            return loss.reshape(())
         loss, _, lse = kl_forward(H, W, idx, logp, chunk, want_loss_tok=False, weight=weight,
                                   reduction=reduction)
         ctx.save_for_backward(H, W, idx, logp, lse, weight)
@@ -270,20 +296,38 @@ class FusedTopKKL(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, grad):
+        if ctx.one_pass:
+            if ctx.spent:
+                raise RuntimeError("fused_kl(one_pass=True) supports one backward per forward")
+            ctx.spent = True
+            dH, dW = ctx.saved_tensors
+            g = grad.reshape(1).to(dtype=torch.float32).contiguous()
+            if dH is not None:
+                scale_(dH, g)
+            if dW is not None:
+                scale_(dW, g)
+                if ctx.w_dtype == torch.bfloat16:
+                    dW = cast_f32_to_bf16(dW)
+            return dH, dW, None, None, None, None, None, None
         H, W, idx, logp, lse, weight = ctx.saved_tensors
         need_dH, need_dW = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
         dH, dW = kl_backward(H, W, idx, logp, lse, grad, ctx.chunk, need_dH=need_dH,
                              need_dW=need_dW, weight=weight, reduction=ctx.reduction)
         if dW is not None and W.dtype == torch.bfloat16:
             dW = cast_f32_to_bf16(dW)
-        return dH, dW, None, None, None, None, None
+        return dH, dW, None, None, None, None, None, None
 
 
 def fused_kl(H: torch.Tensor, W: torch.Tensor, topk_idx: torch.Tensor, topk_logp: torch.Tensor,
              chunk: int = 1024, weight: Optional[torch.Tensor] = None,
-             reduction: str = "sum") -> torch.Tensor:
+             reduction: str = "sum", one_pass: bool = False) -> torch.Tensor:
     """Top-K KL distillation loss, summed (or averaged with ``reduction='mean'``)
     over positions with optional per-position ``weight`` (fp32 [N], e.g. a
-    0/1 mask for packed sequences); differentiable in H and W."""
+    0/1 mask for packed sequences); differentiable in H and W.
+
+    ``one_pass=True`` computes the gradients during the forward, projecting
+    each chunk once instead of twice (about 25% less time for forward plus
+    backward), and holds dH and dW until the backward."""
     _reduction(reduction)
-    return FusedTopKKL.apply(H, W, topk_idx, topk_logp, int(chunk), weight, reduction)
+    return FusedTopKKL.apply(H, W, topk_idx, topk_logp, int(chunk), weight, reduction,
+                             bool(one_pass))

@@ -270,6 +270,17 @@ int kd_fused_kl_check_inputs(const int32_t* topk_idx, const float* topk_logp, in
                              int64_t K, int64_t V, int32_t* flags, void* stream);
 
 /*
+ * x[i] *= s for n values in place, x of `dtype` (KD_F32 or KD_BF16; bf16
+ * values are scaled in float32 and rounded to nearest even), s a float32
+ * DEVICE scalar. When s == 1 the kernel leaves x untouched and costs only
+ * its launch. For callers that obtain the gradients of kd_fused_kl_fwd_bwd
+ * at g = 1 and learn the upstream gradient later (an autograd backward):
+ * scaling by g afterwards gives the gradients at g, bitwise those of the
+ * two-pass calls when g == 1. Device pointers; n >= 0.
+ */
+int kd_scale(void* x, int dtype, int64_t n, const float* s, void* stream);
+
+/*
  * Element-wise float32 -> bfloat16 (round to nearest even) of n values, for
  * callers that keep W in bf16 and want dW in W's dtype. Device pointers;
  * src and dst must not overlap.

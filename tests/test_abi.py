@@ -145,6 +145,17 @@ def test_cast_rejects_invalid(L):
     assert L.kd_cast_f32_to_bf16(vp(FAKE), vp(FAKE), 0, None) == _lib.KD_OK  # nothing to do
 
 
+def test_scale_rejects_invalid(L):
+    vp = ctypes.c_void_p
+    assert L.kd_scale(vp(FAKE), _lib.KD_F32, -1, vp(FAKE), None) == INV
+    assert L.kd_scale(vp(FAKE), 2, 10, vp(FAKE), None) == INV
+    assert L.kd_scale(None, _lib.KD_F32, 10, vp(FAKE), None) == INV
+    assert L.kd_scale(vp(FAKE), _lib.KD_F32, 10, None, None) == INV
+    assert L.kd_scale(vp(FAKE + 2), _lib.KD_F32, 10, vp(FAKE), None) == INV   # fp32 needs 4-byte alignment
+    assert L.kd_scale(vp(FAKE), _lib.KD_F32, 10, vp(FAKE + 1), None) == INV
+    assert L.kd_scale(vp(FAKE), _lib.KD_BF16, 0, vp(FAKE), None) == _lib.KD_OK  # nothing to do
+
+
 def test_binding_fails_loudly_without_gpu_tensors():
     from chunked_kl_loss_chunk_amd import ops
     H = torch.zeros(4, 8)
@@ -325,7 +336,7 @@ int main(void) {
       (fn_t)kd_fused_kl_fwd, (fn_t)kd_fused_kl_bwd,
       (fn_t)kd_fused_kl_fwd_ex, (fn_t)kd_fused_kl_bwd_ex,
       (fn_t)kd_fused_kl_fwd_bwd, (fn_t)kd_teacher_topk,
-      (fn_t)kd_fused_kl_check_inputs, (fn_t)kd_cast_f32_to_bf16,
+      (fn_t)kd_fused_kl_check_inputs, (fn_t)kd_cast_f32_to_bf16, (fn_t)kd_scale,
       (fn_t)kd_timing_enable, (fn_t)kd_timing_read};
   for (unsigned i = 0; i < sizeof(fns) / sizeof(fns[0]); ++i)
     if (!fns[i]) return 3;

@@ -179,6 +179,56 @@ def test_bitwise_deterministic(kd):
     assert a["loss"] == b["loss"]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_autograd_one_pass(kd, dtype):
+    """fused_kl(one_pass=True): with loss.backward() (upstream gradient 1) the
+    gradients are bitwise those of the default two-pass autograd path; with
+    another upstream gradient they match the oracle; a second backward
+    through the same graph is refused."""
+    H, W, idx, logp = _case(300, 96, 2000, 16, dtype, seed=21)
+    Hd, Wd, id_, lp = _to_dev(H, W, idx, logp)
+    grads = []
+    for one_pass in (False, True):
+        h = Hd.clone().requires_grad_(True)
+        w = Wd.clone().requires_grad_(True)
+        loss = kd.fused_kl(h, w, id_, lp, chunk=128, one_pass=one_pass)
+        loss.backward()
+        torch.cuda.synchronize()
+        grads.append((loss.detach(), h.grad, w.grad))
+    (l0, h0, w0), (l1, h1, w1) = grads
+    assert torch.equal(l0, l1) and torch.equal(h0, h1) and torch.equal(w0, w1)
+    assert h1.dtype == Hd.dtype and w1.dtype == Wd.dtype
+
+    h = Hd.clone().requires_grad_(True)
+    w = Wd.clone().requires_grad_(True)
+    g = torch.Generator().manual_seed(22)
+    wt = torch.rand(300, generator=g).to(Hd.device)
+    loss = kd.fused_kl(h, w, id_, lp, chunk=128, weight=wt, reduction="mean", one_pass=True)
+    (0.37 * loss).backward(retain_graph=True)
+    torch.cuda.synchronize()
+    ref = oracle.fused_kl_reference(H, W, idx, logp, grad=0.37, weight=wt.cpu().numpy(),
+                                    reduction="mean")
+    t = TOL[dtype]
+    assert rel_err(loss.item(), ref["loss"]) < t["loss"]
+    assert max_norm_err(h.grad.double().cpu().numpy(), ref["dH"]) < t["grad"]
+    assert max_norm_err(w.grad.double().cpu().numpy(), ref["dW"]) < t["grad"]
+    with pytest.raises(RuntimeError):
+        loss.backward()
+
+
+def test_autograd_one_pass_only_h(kd):
+    # W frozen: only dH is computed and returned.
+    H, W, idx, logp = _case(200, 64, 900, 8, "bf16", seed=23)
+    Hd, Wd, id_, lp = _to_dev(H, W, idx, logp)
+    h = Hd.clone().requires_grad_(True)
+    loss = kd.fused_kl(h, Wd, id_, lp, chunk=64, one_pass=True)
+    loss.backward()
+    torch.cuda.synchronize()
+    ref = oracle.fused_kl_reference(H, W, idx, logp)
+    assert max_norm_err(h.grad.double().cpu().numpy(), ref["dH"]) < TOL["bf16"]["grad"]
+    assert Wd.grad is None
+
+
 # --------------------------------------------------------------------------
 # full size: the 8K-token head (the launch configuration bench.py times) and
 # the gpt-oss head (d = 2880, V = 201,088, 2,048-row chunks)
