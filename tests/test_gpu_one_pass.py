@@ -65,6 +65,8 @@ def test_small_bf16_workload(kd):
     (1100, 96, 3000, 20, "bf16", 128),   # 9 chunks: windows of 4, 4 and 1 chunk
     (1536, 256, 8000, 32, "f32", 512),   # fp32 over 3 chunks of 512 rows
     (90, 64, 10000, 8, "f32", 90),       # a row of 10,000 logits: 2 streaming workgroups, ragged
+    (64, 8, 300, 4, "bf16", 32),         # d = 8: the smallest bf16 row (16 bytes), one partial stage
+    (300, 64, 20000, 16383, "f32", 128), # the largest K (the hit record's 14-bit field), 82% of V cached
 ])
 def test_edge_shapes(kd, N, d, V, K, dtype, chunk):
     H, W, idx, logp = _case(N, d, V, K, dtype, seed=N * 7 + V)

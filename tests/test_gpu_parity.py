@@ -115,6 +115,8 @@ def test_chunk_size_does_not_change_results(kd, chunk):
     (257, 72, 515, 1, "bf16", 128),      # K = 1
     (64, 32, 40, 40, "f32", 16),         # K = V: the full teacher distribution
     (300, 160, 2000, 100, "bf16", 256),  # K = 100 over a small vocabulary
+    (64, 8, 300, 4, "bf16", 32),         # d = 8: the smallest bf16 row (16 bytes), one partial stage
+    (300, 64, 20000, 16383, "f32", 128), # the largest K (the hit record's 14-bit field), 82% of V cached
 ])
 def test_edge_shapes(kd, N, d, V, K, dtype, chunk):
     H, W, idx, logp = _case(N, d, V, K, dtype, seed=N * 7 + V)
