@@ -1066,10 +1066,11 @@ __device__ __forceinline__ uint64_t tk_key(uint2 c) {
   return (uint64_t(fkey(__uint_as_float(c.x))) << 32) | uint64_t(0xFFFFFFFFu - c.y);
 }
 
-// One workgroup per row: the K-th largest key by an 8-bit radix select over
-// the row's candidates, the K keys at or above it gathered (keys are unique,
-// so exactly K), sorted by a bitonic network, and written out with
-// logp = z − lse. The candidates sit in nseg segments of 8192 slots
+// One workgroup per row. With at most kTkMaxK candidates (the usual case)
+// they are all sorted in LDS by a bitonic network; otherwise an 8-bit radix
+// select finds the K-th largest key and the K keys at or above it (keys are
+// unique, so exactly K) are gathered and sorted. The first K are written out
+// with logp = z − lse. The candidates sit in nseg segments of 8192 slots
 // (k_tk_scan); candidate i of the row is found through the segments' prefix
 // sums, kept in LDS.
 constexpr int kTkMaxSegs = int(kMaxTeacherSegs);  // the plan rejects larger vocabularies
@@ -1107,41 +1108,50 @@ __global__ __launch_bounds__(256) void k_tk_finish(const uint2* __restrict__ can
     }
     return list[int64_t(lo) * kDlCols + (i - seg_start[lo])];
   };
-  uint64_t mask = 0;
-  for (int pass = 7; pass >= 0; --pass) {
-    hist[tid] = 0u;
-    __syncthreads();
-    const uint64_t prefix = s_prefix;
-    const int shift = 8 * pass;
+  int m;  // keys gathered into LDS for the sort
+  if (n <= kTkMaxK) {
+    // Few candidates (the usual case: about K + 10): all of them are sorted
+    // and the first K win; no selection pass is needed.
+    for (int i = tid; i < n; i += 256) keys[i] = tk_key(at(i));
+    m = n;
+  } else {
+    uint64_t mask = 0;
+    for (int pass = 7; pass >= 0; --pass) {
+      hist[tid] = 0u;
+      __syncthreads();
+      const uint64_t prefix = s_prefix;
+      const int shift = 8 * pass;
+      for (int i = tid; i < n; i += 256) {
+        const uint64_t key = tk_key(at(i));
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int krem = s_krem, above = 0, bin = 255;
+        for (; bin > 0; --bin) {
+          if (above + int(hist[bin]) >= krem) break;
+          above += int(hist[bin]);
+        }
+        s_krem = krem - above;
+        s_prefix = prefix | (uint64_t(bin) << shift);
+      }
+      mask |= uint64_t(255) << shift;
+      __syncthreads();
+    }
+    const uint64_t kth = s_prefix;
     for (int i = tid; i < n; i += 256) {
       const uint64_t key = tk_key(at(i));
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int krem = s_krem, above = 0, bin = 255;
-      for (; bin > 0; --bin) {
-        if (above + int(hist[bin]) >= krem) break;
-        above += int(hist[bin]);
+      if (key >= kth) {
+        const int slot = atomicAdd(&s_sel, 1);
+        if (slot < kTkMaxK) keys[slot] = key;
       }
-      s_krem = krem - above;
-      s_prefix = prefix | (uint64_t(bin) << shift);
     }
-    mask |= uint64_t(255) << shift;
-    __syncthreads();
-  }
-  const uint64_t kth = s_prefix;
-  for (int i = tid; i < n; i += 256) {
-    const uint64_t key = tk_key(at(i));
-    if (key >= kth) {
-      const int slot = atomicAdd(&s_sel, 1);
-      if (slot < kTkMaxK) keys[slot] = key;
-    }
+    m = K;
   }
   __syncthreads();
   int P = 1;
-  while (P < K) P <<= 1;
-  for (int i = K + tid; i < P; i += 256) keys[i] = 0;
+  while (P < m) P <<= 1;
+  for (int i = m + tid; i < P; i += 256) keys[i] = 0;  // below every real key
   __syncthreads();
   // Bitonic sort of keys[0, P), descending.
   for (int size = 2; size <= P; size <<= 1)
