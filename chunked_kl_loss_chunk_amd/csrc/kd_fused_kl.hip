@@ -970,7 +970,9 @@ __device__ __forceinline__ float fkey_inv(uint32_t k) {
 
 // One wave per row: lse_r from the tile partials (fixed order) and τ_r, the
 // K-th largest tile maximum (bit-by-bit search of its key), or −inf when the
-// vocabulary has fewer than K tiles.
+// vocabulary has fewer than K tiles. Up to 64·kSelectRegs tiles per row
+// (V ≤ 262,144) the keys are searched from registers.
+constexpr int kSelectRegs = 16;
 __global__ __launch_bounds__(256) void k_tk_select(const float2* __restrict__ part, int nVt,
                                                    int rows, int K, float* __restrict__ lse_out,
                                                    float* __restrict__ tau_out) {
@@ -987,13 +989,33 @@ __global__ __launch_bounds__(256) void k_tk_select(const float2* __restrict__ pa
   float tau = kNegInf;
   if (nVt >= K) {
     uint32_t T = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = T | (1u << bit);
-      int n = 0;
-      for (int t = lane; t < nVt; t += 64) n += fkey(pr[t].x) >= c ? 1 : 0;
+    if (nVt <= 64 * kSelectRegs) {
+      // The row's tile-maximum keys stay in registers (0 below every real
+      // key) for the 32 steps of the search.
+      uint32_t key[kSelectRegs];
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) n += __shfl_xor(n, off);
-      if (n >= K) T = c;
+      for (int q = 0; q < kSelectRegs; ++q) {
+        const int t = lane + 64 * q;
+        key[q] = t < nVt ? fkey(pr[t].x) : 0u;
+      }
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = T | (1u << bit);
+        int n = 0;
+#pragma unroll
+        for (int q = 0; q < kSelectRegs; ++q) n += key[q] >= c ? 1 : 0;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) n += __shfl_xor(n, off);
+        if (n >= K) T = c;
+      }
+    } else {
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = T | (1u << bit);
+        int n = 0;
+        for (int t = lane; t < nVt; t += 64) n += fkey(pr[t].x) >= c ? 1 : 0;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) n += __shfl_xor(n, off);
+        if (n >= K) T = c;
+      }
     }
     tau = fkey_inv(T);
   }

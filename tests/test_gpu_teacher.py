@@ -68,6 +68,7 @@ def _inputs(N, d, V, dtype, seed):
     (64, 32, 40, 40, "f32", 16),            # K = V
     (130, 64, 129, 1, "f32", 64),           # K = 1, a one-column last tile
     (200, 96, 3000, 5, "bf16", 1000),       # one chunk, 12 tiles >= K = 5
+    (40, 64, 270000, 100, "bf16", 32),      # 1055 tiles: τ searched from memory, not registers
 ])
 def test_teacher_topk_parity(kd, N, d, V, K, dtype, chunk):
     Ht, Wt = _inputs(N, d, V, dtype, seed=N + V + K)
