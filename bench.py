@@ -11,7 +11,9 @@ Prints ONE JSON line. Besides tokens/s it reports hardware TFLOP/s (8·N·d·V
 per step: forward projection, backward recompute, dH and dW), the pages'
 convention (6·N·d·V, recompute not counted), peak HBM, a roofline entry for the
 dominant kernel measured live with HIP events on the launch stream, and the
-CPU oracle timed on a bounded sample of the same workload.
+CPU oracle timed on a bounded sample of the same workload. The oracle's result
+on that sample is also compared with the GPU outputs of the same rows
+(``oracle_check``: per-token loss, lse and dH at the stated tolerances).
 
     python bench.py [--steps K] [--warmup W] [--workload 8k-head|gpt-oss-head|sweep|small|teacher-cache]
 
@@ -224,7 +226,8 @@ def _host_info():
 
 
 def cpu_baseline(cfg, H, W, idx, logp, rows):
-    """The CPU oracle as it stands, on the first `rows` rows of the workload."""
+    """The CPU oracle as it stands, on the first `rows` rows of the workload.
+    Returns its result (for the oracle check) and the timing record."""
     import numpy as np  # noqa: F401
 
     import oracle
@@ -240,9 +243,9 @@ def cpu_baseline(cfg, H, W, idx, logp, rows):
     Wc = W.cpu()
     _log(f"cpu oracle on {rows} rows, {threads} BLAS threads")
     t0 = time.perf_counter()
-    oracle.fused_kl_reference(Hs, Wc, ids, lps)
+    ref = oracle.fused_kl_reference(Hs, Wc, ids, lps)
     dt = time.perf_counter() - t0
-    return {
+    return ref, {
         "value": rows / dt,
         "unit": "tokens/s",
         "cores": int(threads),
@@ -253,6 +256,36 @@ def cpu_baseline(cfg, H, W, idx, logp, rows):
         "gflops": 6.0 * rows * cfg.d * cfg.V / dt / 1e9,
         **_host_info(),
     }
+
+
+def oracle_check(cfg, H, W, idx, logp, ref, rows):
+    """The GPU path in the bench's launch configuration (full workload, its
+    chunk size) against the oracle on the sampled rows: per-token loss and lse
+    (relative) and dH (max-normalised). Each of these rows depends only on its
+    own inputs; dW sums over all rows and is covered by the tests' identities."""
+    import numpy as np
+    import torch
+
+    import chunked_kl_loss_chunk_amd as kd
+
+    g = torch.ones(1, dtype=torch.float32, device=H.device)
+    _, loss_tok, lse = kd.kl_forward(H, W, idx, logp, cfg.chunk, want_loss_tok=True)
+    dH, _ = kd.kl_backward(H, W, idx, logp, lse, g, cfg.chunk, need_dW=False)
+    torch.cuda.synchronize()
+    lt = loss_tok[:rows].double().cpu().numpy()
+    ls = lse[:rows].double().cpu().numpy()
+    dh = dH[:rows].double().cpu().numpy()
+    del dH
+    e_loss = float(np.abs(lt - ref["loss_tok"]).max() / max(np.abs(ref["loss_tok"]).max(), 1e-30))
+    e_sum = float(abs(lt.sum() - ref["loss"]) / max(abs(ref["loss"]), 1e-30))
+    e_lse = float((np.abs(ls - ref["lse"]) / np.maximum(np.abs(ref["lse"]), 1e-30)).max())
+    e_dh = float(np.abs(dh - ref["dH"]).max() / max(np.abs(ref["dH"]).max(), 1e-30))
+    tol_loss, tol_grad = (2e-3, 2e-2) if cfg.dtype == "bf16" else (1e-4, 1e-4)
+    return {"rows": rows, "loss_tok_max_norm_err": e_loss, "loss_sum_rel_err": e_sum,
+            "lse_max_rel_err": e_lse, "dH_max_norm_err": e_dh,
+            "tolerance": {"loss": tol_loss, "grad": tol_grad},
+            "pass": bool(e_loss < tol_loss and e_sum < tol_loss and e_lse < tol_loss
+                         and e_dh < tol_grad)}
 
 
 def run_teacher_cache(steps, warmup, dev, no_cpu, cpu_rows):
@@ -462,7 +495,10 @@ def main():
     }
     if not args.no_cpu_baseline:
         H, W, idx, logp = r["inputs"]
-        out["cpu_baseline"] = cpu_baseline(cfg, H, W, idx, logp, min(args.cpu_rows, N))
+        rows = min(args.cpu_rows, N)
+        ref, out["cpu_baseline"] = cpu_baseline(cfg, H, W, idx, logp, rows)
+        out["oracle_check"] = oracle_check(cfg, H, W, idx, logp, ref, rows)
+        del ref
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
