@@ -156,6 +156,13 @@ def test_scale_rejects_invalid(L):
     assert L.kd_scale(vp(FAKE), _lib.KD_BF16, 0, vp(FAKE), None) == _lib.KD_OK  # nothing to do
 
 
+def test_timing_flag_and_read_validated(L):
+    assert L.kd_timing_enable(2) == INV
+    assert L.kd_timing_enable(-1) == INV
+    assert L.kd_timing_read(None, None) == INV
+    assert L.kd_timing_enable(0) == _lib.KD_OK
+
+
 def test_binding_fails_loudly_without_gpu_tensors():
     from chunked_kl_loss_chunk_amd import ops
     H = torch.zeros(4, 8)
