@@ -65,6 +65,19 @@ def _kernel_stats(kd_lib):
 TRAFFIC_WORKLOAD = "llama3.2b-head-8k"  # the workload profiles/hbm_traffic.md was taken on
 
 
+def source_sha256() -> str:
+    """sha-256 over the kernel sources (the files of csrc, in sorted order):
+    names the kernel version a bench line or a profile was taken on."""
+    import hashlib
+
+    src = os.path.join(ROOT, "chunked_kl_loss_chunk_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(src)):
+        with open(os.path.join(src, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def _traffic(kernel: str, workload_name: str = TRAFFIC_WORKLOAD):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on this workload and on the current kernel source; else None."""
@@ -73,16 +86,9 @@ def _traffic(kernel: str, workload_name: str = TRAFFIC_WORKLOAD):
     path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
     if not os.path.exists(path):
         return None
-    import hashlib
-
-    src = os.path.join(ROOT, "chunked_kl_loss_chunk_amd", "csrc")
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(src)):
-        with open(os.path.join(src, f), "rb") as fh:
-            h.update(fh.read())
     text = open(path).read()
     m = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
-    if not m or m.group(1) != h.hexdigest():
+    if not m or m.group(1) != source_sha256():
         return None
     row = re.search(rf"^\|\s*{kernel}\s*\|[^|]*\|[^|]*\|\s*([0-9.eE+]+)\s*\|", text, re.M)
     return float(row.group(1)) if row else None
@@ -367,6 +373,7 @@ def run_teacher_cache(steps, warmup, dev, no_cpu, cpu_rows):
         "torch_reference": {"ms_per_step": s_torch * 1e3, "tokens_per_s": N / s_torch,
                             "what": "bf16 matmul per 1024 rows, fp32 log_softmax, torch.topk"},
         "cpu_baseline": None,
+        "kernel_source_sha256": source_sha256(),
     }
     if not no_cpu:
         import oracle
@@ -477,6 +484,7 @@ def main():
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": _traffic(dom, cfg.name)},
         "cache_sha256": r["cache_sha256"],
+        "kernel_source_sha256": source_sha256(),
     }
     one = r["one_pass"]
     s1 = one["sec_per_step"]
