@@ -1,8 +1,9 @@
 """Plain, slow, dense fp64 oracle of the top-K KL distillation loss.
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
-and the CPU-baseline leg of ``bench.py``; never by the HIP library or its
-binding. It shares no code, table or helper with the GPU path.
+and the CPU-baseline leg of ``bench.py`` (which also compares the result of
+its sample with the GPU outputs of the same rows); never by the HIP library
+or its binding. It shares no code, table or helper with the GPU path.
 
 Source pages (cited by title and section):
 

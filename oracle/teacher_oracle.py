@@ -1,7 +1,8 @@
 """Plain fp64 oracle of the offline teacher cache: top-K ids and log-probs.
 
 TEST INFRASTRUCTURE ONLY (same rule as kl_oracle.py): imported by ``tests/``
-and never by the HIP library or its binding.
+and by the CPU-baseline leg of ``bench.py --workload teacher-cache``, never by
+the HIP library or its binding.
 
 Source pages (cited by title and section):
 
