@@ -93,3 +93,54 @@ def test_one_pass_graph_replays_equal_eager(kd, dtype, weighted):
         torch.cuda.synchronize()
         for name, a, b in zip(("loss", "loss_tok", "lse", "dH", "dW"), outs, ref):
             assert torch.equal(a, b), (rep, name)
+
+
+def test_teacher_cache_cast_and_scale_graph_replays_equal_eager(kd):
+    """The teacher cache producer, the fp32 -> bf16 cast and the in-place
+    scale captured once (every launch on the capturing stream, no memset
+    nodes); each replay on new inputs equals eager calls on them bit for bit."""
+    dev = torch.device("cuda:0")
+    N, d, V, K, chunk = 600, 64, 3000, 12, 256
+
+    def draw(seed):
+        g = torch.Generator().manual_seed(seed)
+        Ht = torch.randn(N, d, generator=g).to(torch.bfloat16)
+        Wt = (torch.randn(V, d, generator=g) * 2 * d ** -0.5).to(torch.bfloat16)
+        x = torch.randn(N, 136, generator=g)
+        y = torch.randn(N, 72, generator=g).to(torch.bfloat16)
+        return Ht.to(dev), Wt.to(dev), x.to(dev), y.to(dev)
+
+    Ht, Wt, x, y0 = draw(91)
+    y = y0.clone()
+    s = torch.full((1,), 0.5, dtype=torch.float32, device=dev)
+
+    def run():
+        idx, logp, lse = kd.teacher_topk(Ht, Wt, K, chunk)
+        xb = kd.cast_f32_to_bf16(x)
+        kd.scale_(y, s)
+        return idx, logp, lse, xb
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = run()
+    for rep in range(3):
+        Hn, Wn, xn, yn = draw(92 + rep)
+        Ht.copy_(Hn)
+        Wt.copy_(Wn)
+        x.copy_(xn)
+        y.copy_(yn)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in outs] + [y.clone()]
+        y.copy_(yn)
+        ref = list(run()) + [y]
+        torch.cuda.synchronize()
+        for name, a, b in zip(("idx", "logp", "lse", "cast", "scale"), got, ref):
+            assert torch.equal(a, b), (rep, name)
