@@ -140,11 +140,11 @@ def run_gpu(cfg, steps, warmup, dev):
     _log(f"timing {steps} steps")
     torch.cuda.reset_peak_memory_stats(dev)
     resident = torch.cuda.memory_allocated(dev)
-    L.kd_timing_enable(1)
-    _kernel_stats(L)  # clear
-    # Events on the stream the library launches on (torch's current stream)
-    # between steps give per-step times for the median; the wall clock around
-    # all steps gives the reported mean.
+    # The reported loop runs with the library's kernel timing off: no events
+    # between the launches of a step. Events on the stream the library
+    # launches on (torch's current stream) between steps give per-step times
+    # for the median; the wall clock around all steps gives the reported mean.
+    L.kd_timing_enable(0)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -154,11 +154,22 @@ def run_gpu(cfg, steps, warmup, dev):
         ev[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kstats = _kernel_stats(L)
-    L.kd_timing_enable(0)
     per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     median_ms = per_step[steps // 2] if steps % 2 else 0.5 * (per_step[steps // 2 - 1] + per_step[steps // 2])
     peak = torch.cuda.max_memory_allocated(dev)
+    # A second loop of the same steps with every launch bracketed by HIP
+    # events on its stream: the per-class kernel times and the roofline entry.
+    _log(f"timing {steps} instrumented steps (per-kernel events)")
+    L.kd_timing_enable(1)
+    _kernel_stats(L)  # clear
+    torch.cuda.synchronize()
+    i0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    i1 = time.perf_counter()
+    kstats = _kernel_stats(L)
+    L.kd_timing_enable(0)
     # The forward and the backward pass, each timed alone.
     _, _, lse = kd.kl_forward(H, W, idx, logp, cfg.chunk, want_loss_tok=False)
     torch.cuda.synchronize()
@@ -197,6 +208,7 @@ def run_gpu(cfg, steps, warmup, dev):
     one = _time_one_pass(kd, L, H, W, idx, logp, g, dW, cfg.chunk, steps, warmup, dev)
     return {
         "sec_per_step": (t1 - t0) / steps,
+        "instrumented_sec_per_step": (i1 - i0) / steps,
         "median_ms_per_step": median_ms,
         "fwd_sec_per_step": (f1 - f0) / steps,
         "bwd_sec_per_step": (b1 - f1) / steps,
@@ -420,12 +432,140 @@ def run_teacher_cache(steps, warmup, dev, no_cpu, cpu_rows):
     print(json.dumps(out), flush=True)
 
 
+def sweep_fit(lines):
+    """Least-squares a + b·N over the sweep's points, for peak HBM (b in bytes
+    per token) and for the step time (b in µs per token), with the residual
+    of every point: linear growth in N shows as residuals that are small
+    against the values."""
+    import numpy as np
+
+    N = np.array([float(l["N"]) for l in lines])
+    A = np.stack([np.ones_like(N), N], axis=1)
+    out = {"N": [int(n) for n in N]}
+    for key, scale, unit in (("peak_hbm_bytes", 1.0, "bytes"), ("ms_per_step", 1e3, "us"),
+                             ("one_pass_peak_hbm_bytes", 1.0, "bytes")):
+        y = np.array([float(l[key]) for l in lines])
+        (a, b), *_ = np.linalg.lstsq(A, y, rcond=None)
+        res = y - (a + b * N)
+        out[key] = {"a": float(a), "b_per_token": float(b * scale), "unit_b": f"{unit}/token",
+                    "residuals": [float(x) for x in res],
+                    "max_rel_residual": float(np.max(np.abs(res) / np.abs(y)))}
+    return out
+
+
+def run_gemm_ceiling(steps, warmup, dev):
+    """torch's bf16 matmul (hipBLASLt) on the three contraction shapes of the
+    8K head, with the bench's seeded operands, beside the fused kernels' own
+    per-launch times measured in the same process on the same inputs:
+
+      chunk logits  [1024 x 3072] . [3072 x 128256]   (forward; recomputed in the backward)
+      window dH     [4096 x 128256] . [128256 x 3072]
+      window dW     [128256 x 4096] . [4096 x 3072]   (float32 output where torch offers it)
+
+    The dlogits operand of dH and dW is the real one for the first 4096 rows
+    (S_r q − p at the cached ids, rounded to bf16), formed here with torch."""
+    import torch
+
+    import chunked_kl_loss_chunk_amd as kd
+    import workload
+
+    cfg = workload.config(3)
+    L = kd.lib()
+    H, W, idx, logp, _ = _gen(cfg, dev)
+    C, win = cfg.chunk, 4 * cfg.chunk
+    Hc = H[:C].contiguous()
+    Hw = H[:win].contiguous()
+    with torch.no_grad():
+        z = (Hw @ W.T).float()
+        q = torch.softmax(z, dim=1)
+        del z
+        p = torch.exp(logp[:win])
+        dl = q * p.sum(dim=1, keepdim=True)
+        del q
+        dl.scatter_add_(1, idx[:win].long(), -p)
+        dl = dl.to(torch.bfloat16)
+        dlT = dl.t().contiguous()
+    torch.cuda.synchronize()
+
+    def mm_f32(a, b):
+        try:
+            return torch.mm(a, b, out_dtype=torch.float32)
+        except (TypeError, RuntimeError):
+            return torch.mm(a, b)
+
+    cases = {
+        "logits (H_c . W^T)": (lambda: torch.mm(Hc, W.t()), 2.0 * C * cfg.d * cfg.V),
+        "logits (W . H_c^T)": (lambda: torch.mm(W, Hc.t()), 2.0 * C * cfg.d * cfg.V),
+        "dH (dl . W)": (lambda: torch.mm(dl, W), 2.0 * win * cfg.d * cfg.V),
+        "dW (dl^T . H_w, fp32 out)": (lambda: mm_f32(dlT, Hw), 2.0 * win * cfg.d * cfg.V),
+        "dW (dl^T . H_w, bf16 out)": (lambda: torch.mm(dlT, Hw), 2.0 * win * cfg.d * cfg.V),
+    }
+    reps = max(steps, 5)
+    lib_ms = {}
+    for name, (fn, flops) in cases.items():
+        for _ in range(max(warmup, 2)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        lib_ms[name] = {"ms": ms, "tflops": flops / ms / 1e9, "frac_of_peak": flops / ms / 1e9 / PEAK_BF16_TFLOPS}
+        _log(f"{name}: {ms:.3f} ms")
+    del dl, dlT
+    torch.cuda.empty_cache()
+
+    # The fused kernels on the same inputs, same process: per-launch HIP-event
+    # times of a full forward + backward step.
+    g = torch.ones(1, dtype=torch.float32, device=dev)
+    dW = torch.empty((cfg.V, cfg.d), dtype=torch.float32, device=dev)
+
+    def step():
+        _, _, lse = kd.kl_forward(H, W, idx, logp, cfg.chunk, want_loss_tok=False)
+        kd.kl_backward(H, W, idx, logp, lse, g, cfg.chunk, dW_out=dW, accumulate=False)
+
+    for _ in range(max(warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    L.kd_timing_enable(1)
+    _kernel_stats(L)
+    for _ in range(reps):
+        step()
+    torch.cuda.synchronize()
+    ks = _kernel_stats(L)
+    L.kd_timing_enable(0)
+    fused = {k: ks[k]["total_ms"] / ks[k]["launches"] for k in
+             ("fwd_logits", "bwd_dlogits", "bwd_dh", "bwd_dw") if ks[k]["launches"]}
+    best_logits = min(lib_ms["logits (H_c . W^T)"]["ms"], lib_ms["logits (W . H_c^T)"]["ms"])
+    ratio = {
+        "fwd_logits / best logits GEMM": fused["fwd_logits"] / best_logits,
+        "bwd_dlogits / best logits GEMM": fused["bwd_dlogits"] / best_logits,
+        "bwd_dh / dH GEMM": fused["bwd_dh"] / lib_ms["dH (dl . W)"]["ms"],
+        "bwd_dw / dW GEMM (fp32 out)": fused["bwd_dw"] / lib_ms["dW (dl^T . H_w, fp32 out)"]["ms"],
+    }
+    print(json.dumps({
+        "what": "hipBLASLt (torch.mm, bf16 operands) on the fused loss's contraction shapes, "
+                "8K head, beside the fused kernels in the same process",
+        "config": {"workload": cfg.name, "N": cfg.N, "d": cfg.d, "V": cfg.V, "chunk": C,
+                   "window": win},
+        "torch_mm": lib_ms,
+        "fused_avg_ms_per_launch": fused,
+        "fused_over_library": ratio,
+        "reps": reps,
+        "kernel_source_sha256": source_sha256(),
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="8k-head", choices=[*WORKLOADS, "sweep", "teacher-cache"])
+    ap.add_argument("--workload", default="8k-head",
+                    choices=[*WORKLOADS, "sweep", "teacher-cache", "gemm-ceiling"])
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -446,22 +586,32 @@ def main():
                           min(args.cpu_rows, 1024))
         return
     if args.workload == "sweep":
+        lines = []
         for N in workload.SWEEP_N:
             cfg = workload.config(4, N=N)
             r = run_gpu(cfg, args.steps, args.warmup, dev)
             s = r["sec_per_step"]
-            print(json.dumps({
+            line = {
                 "workload": cfg.name, "N": N, "d": cfg.d, "V": cfg.V, "K": cfg.K, "chunk": cfg.chunk,
                 "ms_per_step": s * 1e3, "tokens_per_s": N / s,
                 "tflops": 8 * N * cfg.d * cfg.V / s / 1e12,
+                "frac_of_peak": 8 * N * cfg.d * cfg.V / s / 1e12 / PEAK_BF16_TFLOPS,
                 "one_pass_ms_per_step": r["one_pass"]["sec_per_step"] * 1e3,
                 "one_pass_tokens_per_s": N / r["one_pass"]["sec_per_step"],
                 "peak_hbm_bytes": r["peak_hbm_bytes"], "resident_bytes": r["resident_bytes"],
                 "peak_hbm_gib": r["peak_hbm_bytes"] / 2**30,
+                "one_pass_peak_hbm_bytes": r["one_pass"]["peak_hbm_bytes"],
                 "pages_context": PAGES_CONTEXT_SWEEP.get(N),
-            }), flush=True)
+                "kernel_source_sha256": source_sha256(),
+            }
+            lines.append(line)
+            print(json.dumps(line), flush=True)
             del r
             torch.cuda.empty_cache()
+        print(json.dumps({"sweep_fit": sweep_fit(lines)}), flush=True)
+        return
+    if args.workload == "gemm-ceiling":
+        run_gemm_ceiling(args.steps, args.warmup, dev)
         return
 
     cid, _ = WORKLOADS[args.workload]
@@ -503,6 +653,7 @@ def main():
         "resident_input_bytes": r["resident_bytes"],
         "kernels": kernels_out,
         "median_ms_per_step": r["median_ms_per_step"],
+        "instrumented_ms_per_step": r["instrumented_sec_per_step"] * 1e3,
         "fwd_ms_per_step": r["fwd_sec_per_step"] * 1e3,
         "bwd_ms_per_step": r["bwd_sec_per_step"] * 1e3,
         "graph_ms_per_step": None if r["graph_sec_per_step"] is None else r["graph_sec_per_step"] * 1e3,

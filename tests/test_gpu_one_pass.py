@@ -67,6 +67,8 @@ def test_small_bf16_workload(kd):
     (90, 64, 10000, 8, "f32", 90),       # a row of 10,000 logits: 2 streaming workgroups, ragged
     (64, 8, 300, 4, "bf16", 32),         # d = 8: the smallest bf16 row (16 bytes), one partial stage
     (300, 64, 20000, 16383, "f32", 128), # the largest K (the hit record's 14-bit field), 82% of V cached
+    (260, 320, 1100, 9, "bf16", 128),    # d = 320: one full 256-wide d tile and a 64-wide one
+    (300, 2880, 1500, 20, "bf16", 128),  # d = 2880 (the gpt-oss head): 11 full d tiles + 64 columns
 ])
 def test_edge_shapes(kd, N, d, V, K, dtype, chunk):
     H, W, idx, logp = _case(N, d, V, K, dtype, seed=N * 7 + V)

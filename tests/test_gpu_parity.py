@@ -117,6 +117,8 @@ def test_chunk_size_does_not_change_results(kd, chunk):
     (300, 160, 2000, 100, "bf16", 256),  # K = 100 over a small vocabulary
     (64, 8, 300, 4, "bf16", 32),         # d = 8: the smallest bf16 row (16 bytes), one partial stage
     (300, 64, 20000, 16383, "f32", 128), # the largest K (the hit record's 14-bit field), 82% of V cached
+    (260, 320, 1100, 9, "bf16", 128),    # d = 320: one full 256-wide d tile and a 64-wide one
+    (300, 2880, 1500, 20, "bf16", 128),  # d = 2880 (the gpt-oss head): 11 full d tiles + 64 columns
 ])
 def test_edge_shapes(kd, N, d, V, K, dtype, chunk):
     H, W, idx, logp = _case(N, d, V, K, dtype, seed=N * 7 + V)
@@ -281,33 +283,65 @@ def test_full_size_gradient_identities(head8k):
     assert abs(a - b) < 2e-2 * max(abs(a), abs(b), 1e-12)
 
 
+def sampled_vocab_ids(cfg, idx, seed):
+    """Vocabulary entries whose dW rows are compared: cached ids of the first
+    rows, random ids, and the first and last entries."""
+    rng = np.random.default_rng(seed)
+    hit_ids = np.unique(idx[:64].numpy().reshape(-1))
+    return np.unique(np.concatenate([hit_ids[:8], rng.integers(0, cfg.V, 8), [0, cfg.V - 1]]))
+
+
+def oracle_dw_rows(H, W, idx, logp, J, block=256):
+    """dW[J, :] from the oracle's dlogits, assembled over every row of the
+    workload in row blocks. dW sums over all rows; the blocks are independent,
+    so they run in a pool of threads (numpy's elementwise work is single
+    threaded; BLAS threads are shared out among the workers) and their
+    partial sums are added in block order."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    N = H.shape[0]
+    W64 = oracle.to_f64(W)
+    H64 = oracle.to_f64(H)
+    ncpu = len(os.sched_getaffinity(0))
+    workers = max(1, min(8, ncpu // 2))
+
+    def one(r0):
+        rows = np.arange(r0, min(N, r0 + block))
+        part = oracle.rows_reference(H, W64, idx, logp, rows, with_dh=False)
+        return part["dlogits"][:, J].T @ H64[rows]
+
+    with threadpool_limits(limits=max(1, ncpu // workers), user_api="blas"):
+        with ThreadPoolExecutor(workers) as ex:
+            parts = list(ex.map(one, range(0, N, block)))
+    ref = np.zeros((len(J), H.shape[1]))
+    for p in parts:
+        ref += p
+    return ref
+
+
 @pytest.mark.timeout(1200)
 def test_full_size_sampled_dw_rows(head8k):
     """dW rows (vocabulary entries) against the oracle's dlogits assembled
-    over all 8192 rows in blocks of one chunk."""
+    over all 8192 rows."""
     cfg, (H, W, idx, logp), got = head8k
-    rng = np.random.default_rng(32)
-    hit_ids = np.unique(idx[:64].numpy().reshape(-1))
-    J = np.unique(np.concatenate([hit_ids[:8], rng.integers(0, cfg.V, 8), [0, cfg.V - 1]]))
-    W64 = oracle.to_f64(W)
-    H64 = oracle.to_f64(H)
-    ref = np.zeros((len(J), cfg.d))
-    for r0 in range(0, cfg.N, cfg.chunk):
-        rows = np.arange(r0, min(cfg.N, r0 + cfg.chunk))
-        part = oracle.rows_reference(H, W64, idx, logp, rows, with_dh=False)
-        ref += part["dlogits"][:, J].T @ H64[rows]
-        del part
+    J = sampled_vocab_ids(cfg, idx, 32)
+    ref = oracle_dw_rows(H, W, idx, logp, J)
     assert max_norm_err(got["dW"][J], ref) < 2e-2
 
 
 # --------------------------------------------------------------------------
 # full size at the other configurations: the gpt-oss head (d = 2880 leaves a
 # ragged d tile; V = 201,088) and the longest point of the long-context sweep
-# (N = 262,144 in 2,048-row chunks: four prep groups, 64 dW windows). The
-# oracle checks sampled rows; dW is checked through identities that hold at
-# any size, computed on the GPU in float64.
+# (N = 32,768 and 262,144 in 2,048-row chunks: up to four prep groups and 64
+# dW windows). The oracle checks sampled rows; dW is checked through
+# identities that hold at any size, computed on the GPU in float64, and, at
+# the gpt-oss head and the 32,768-token point, on sampled dW rows over all d
+# columns against the oracle's dlogits assembled over every row.
 # --------------------------------------------------------------------------
-def _full_size_check(kd, cfg, rows_extra):
+def _full_size_check(kd, cfg, rows_extra, dw_rows=False):
     H, W, idx, logp = workload.make_inputs(cfg, teacher_device="cuda")
     Hd, Wd, id_, lp = _to_dev(H, W, idx, logp)
     loss_sum, loss_tok, lse = kd.kl_forward(Hd, Wd, id_, lp, cfg.chunk)
@@ -329,21 +363,35 @@ def _full_size_check(kd, cfg, rows_extra):
     a = (dW64 * Wd.double()).sum().item()
     b = (dH.double() * Hd.double()).sum().item()
     assert abs(a - b) < 2e-2 * max(abs(a), abs(b), 1e-12)
+    del dW64
+    if dw_rows:
+        J = sampled_vocab_ids(cfg, idx, cfg.N + 7)
+        got = dW[torch.tensor(J, device=Hd.device)].double().cpu().numpy()
+        del Hd, Wd, id_, lp, dH, dW
+        torch.cuda.empty_cache()
+        ref = oracle_dw_rows(H, W, idx, logp, J)
+        assert max_norm_err(got, ref) < 2e-2
+        # the last d tile on its own (columns past the last multiple of 256)
+        tail = (cfg.d // 256) * 256
+        if tail < cfg.d:
+            assert np.abs(got[:, tail:] - ref[:, tail:]).max() < 2e-2 * np.abs(ref).max()
 
 
-@pytest.mark.timeout(900)
+@pytest.mark.timeout(1200)
 def test_full_size_gpt_oss_head(kd):
     cfg = workload.config(5)
-    _full_size_check(kd, cfg, [0, 2047, 2048, 16383, cfg.N - 1])
+    _full_size_check(kd, cfg, [0, 2047, 2048, 16383, cfg.N - 1], dw_rows=True)
     torch.cuda.empty_cache()
 
 
-@pytest.mark.timeout(900)
+@pytest.mark.timeout(1200)
 @pytest.mark.parametrize("N", [workload.SWEEP_N[0], workload.SWEEP_N[-1]])
 def test_full_size_long_context(kd, N):
     cfg = workload.config(4, N=N)
     extra = [0, 2047, 2048, 4095, 4096, N // 2, N - 1]
     if N > 65536:
         extra += [65535, 65536, 131071, 196608]  # prep-group boundaries
-    _full_size_check(kd, cfg, extra)
+    # element-wise dW rows where the oracle's pass over every row takes a few
+    # minutes; at 262,144 tokens only the identities
+    _full_size_check(kd, cfg, extra, dw_rows=N <= 32768)
     torch.cuda.empty_cache()

@@ -409,3 +409,44 @@ def test_planted_unweighted_gradient_is_caught():
     eH = [(i, j) for i in range(4) for j in range(3)]
     eW = [(i, j) for i in range(7) for j in range(3)]
     assert _fd_errors(broken, H, W, idx, logp, 1.0, eH, eW) > 1e-3
+
+
+# --------------------------------------------------------------------------
+# the exact upcast of bf16 inputs
+# --------------------------------------------------------------------------
+def _bf16_value(bits: int) -> float:
+    """The value of a bfloat16 bit pattern, decoded from its fields: 1 sign
+    bit, 8 exponent bits (bias 127), 7 fraction bits; exponent 0 is a
+    subnormal (or zero) and exponent 255 infinity or NaN."""
+    sign = -1.0 if bits & 0x8000 else 1.0
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    if e == 0xFF:
+        return sign * math.inf if f == 0 else math.nan
+    if e == 0:
+        return sign * math.ldexp(f, -126 - 7)
+    return sign * math.ldexp(128 + f, e - 127 - 7)
+
+
+def test_to_f64_bf16_is_exact():
+    """to_f64 of a bfloat16 tensor gives exactly the value each bit pattern
+    encodes: zeros of both signs, the smallest and largest subnormals, the
+    smallest normal, 1, the largest finite value, infinities, and every
+    pattern with a fraction of all ones or a single one."""
+    special = [0x0000, 0x8000, 0x0001, 0x807F, 0x0080, 0x3F80, 0xBF80, 0x7F7F, 0xFF7F,
+               0x7F80, 0xFF80, 0x4049, 0x3E80]
+    special += [(s << 15) | (e << 7) | f for s in (0, 1) for e in range(255)
+                for f in (0x7F, 0x01, 0x40)]
+    rng = np.random.default_rng(5)
+    special += [int(b) for b in rng.integers(0, 1 << 16, 4000) if ((b >> 7) & 0xFF) != 0xFF]
+    bits = np.array(special, dtype=np.uint16)
+    t = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+    got = oracle.to_f64(t)
+    want = np.array([_bf16_value(int(b)) for b in bits])
+    assert got.dtype == np.float64 and got.shape == want.shape
+    assert np.array_equal(got, want)
+    # signs of zero survive as well
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+    # and a 2-D bf16 operand keeps its shape and row order
+    m = t[:4000].reshape(40, 100)
+    assert np.array_equal(oracle.to_f64(m), want[:4000].reshape(40, 100))
