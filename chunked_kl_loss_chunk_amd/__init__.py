@@ -15,6 +15,7 @@ from .ops import (  # noqa: F401
     kl_backward,
     kl_forward,
     kl_forward_backward,
+    kl_forward_noalloc,
     scale_,
     teacher_topk,
     workspace_bytes,

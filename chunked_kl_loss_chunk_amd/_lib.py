@@ -15,6 +15,7 @@ KD_F32, KD_BF16 = 0, 1
 KD_PASS_FWD, KD_PASS_BWD, KD_PASS_TEACHER, KD_PASS_FWD_BWD = 0, 1, 2, 3
 KD_REDUCE_SUM, KD_REDUCE_MEAN = 0, 1
 KD_CHECK_ID_RANGE, KD_CHECK_DUPLICATE, KD_CHECK_LOGP = 1, 2, 4
+KD_NOALLOC_SCRATCH_BYTES = 64 << 20  # the library-held scratch of kd_fused_kl_fwd_noalloc
 
 # Every function the header declares, with (restype, argtypes).
 _vp, _i64, _i, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
@@ -29,6 +30,8 @@ SIGNATURES = {
                                 _vp, _vp, _vp, _vp, _sz, _vp]),
     "kd_fused_kl_bwd_ex": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _i64, _i64, _i64, _i64,
                                 _i64, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
+    "kd_fused_kl_fwd_noalloc": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _i64, _i64, _i64, _i64,
+                                     _i64, _vp, _vp, _vp, _vp]),
     "kd_fused_kl_fwd_bwd": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _i64, _i64, _i64, _i64, _i64,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
     "kd_teacher_topk": (_i, [_vp, _vp, _i, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz,

@@ -39,6 +39,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -1287,9 +1288,13 @@ hipEvent_t timing_event() {
   return g_event_pool[g_events_used++];
 }
 
+// Set while the no-allocation entry point runs on this thread: its launches
+// are not bracketed by events (creating one may allocate).
+thread_local bool t_no_events = false;
+
 template <class F>
 void timed(int cls, hipStream_t st, F&& launch) {
-  if (!g_timing) {
+  if (!g_timing || t_no_events) {
     launch();
     return;
   }
@@ -1642,6 +1647,39 @@ int run_teacher(const Plan& p, const void* Ht, const void* Wt, int32_t* idx, flo
 
 inline bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
+// --------------------------------------------------------------------------
+// library-held scratch of the no-allocation forward entry point
+// --------------------------------------------------------------------------
+// Every GPU the library runs on holds its own copy of this array from the
+// moment the code object is loaded until the process ends. In host code the
+// name is only a handle: its device address on the current device comes from
+// hipGetSymbolAddress, looked up once per device and kept in g_scratch_ptr.
+static __device__ __align__(256) char scratch[KD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's copy of `scratch`.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KD_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return KD_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KD_OK;
+}
+
+struct NoEventsScope {
+  NoEventsScope() { t_no_events = true; }
+  ~NoEventsScope() { t_no_events = false; }
+};
+
 }  // namespace
 }  // namespace kd
 
@@ -1693,6 +1731,30 @@ int kd_fused_kl_fwd_ex(const void* H, const void* W, int dtype, const int32_t* t
                                               loss, workspace, s)
                           : kd::run_fwd<false>(p, H, W, topk_idx, topk_logp, w, mean, loss_tok, lse,
                                                loss, workspace, s);
+}
+
+int kd_fused_kl_fwd_noalloc(const void* H, const void* W, int dtype, const int32_t* topk_idx,
+                            const float* topk_logp, const float* weight, int reduction,
+                            int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk,
+                            float* loss_tok, float* lse, float* loss, void* stream) {
+  kd::Plan p;
+  const int st = kd::make_plan(KD_PASS_FWD, N, d, V, K, chunk, dtype, &p);
+  if (st != KD_OK) return st;
+  if (p.total > KD_NOALLOC_SCRATCH_BYTES) return KD_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return KD_ERR_HIP;
+  if (s != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return KD_ERR_INVALID_ARG;
+    if (int(sdev) != cur) return KD_ERR_INVALID_ARG;
+  }
+  void* ws = nullptr;
+  const int got = kd::scratch_on_current_device(&ws);
+  if (got != KD_OK) return got;
+  kd::NoEventsScope no_events;
+  return kd_fused_kl_fwd_ex(H, W, dtype, topk_idx, topk_logp, weight, reduction, N, d, V, K, chunk,
+                            loss_tok, lse, loss, ws, KD_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int kd_fused_kl_fwd(const void* H, const void* W, int dtype, const int32_t* topk_idx,

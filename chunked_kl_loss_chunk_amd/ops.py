@@ -108,6 +108,32 @@ def kl_forward(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, logp: torch.
     return loss_sum, loss_tok, lse
 
 
+def kl_forward_noalloc(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor,
+                       logp: torch.Tensor, chunk: int, loss: torch.Tensor,
+                       lse: torch.Tensor, loss_tok: Optional[torch.Tensor] = None,
+                       weight: Optional[torch.Tensor] = None, reduction: str = "sum") -> None:
+    """kd_fused_kl_fwd_noalloc: the forward pass into caller-provided outputs,
+    with the library's own scratch instead of a workspace. Nothing is
+    allocated here or in the library: ``loss`` ([1] fp32), ``lse`` ([N] fp32)
+    and ``loss_tok`` ([N] fp32 or None) are written on the current stream.
+    Sizes whose forward workspace exceeds KD_NOALLOC_SCRATCH_BYTES raise."""
+    N, d, V, K = _check_inputs(H, W, idx, logp)
+    dev = H.device
+    dt = dtype_code(H.dtype)
+    red = _reduction(reduction)
+    weight = _check_weight(weight, N, dev)
+    for name, t, n in (("loss", loss, 1), ("lse", lse, N), ("loss_tok", loss_tok, N)):
+        if t is None and name == "loss_tok":
+            continue
+        if (t.shape != (n,) or t.dtype != torch.float32 or not t.is_contiguous()
+                or t.device != dev):
+            raise ValueError(f"{name} must be a contiguous fp32 [{n}] tensor on the inputs' device")
+    st = _lib.lib().kd_fused_kl_fwd_noalloc(_p(H), _p(W), dt, _p(idx), _p(logp), _p(weight), red,
+                                             N, d, V, K, chunk, _p(loss_tok), _p(lse), _p(loss),
+                                             _stream(dev))
+    _lib.check("kd_fused_kl_fwd_noalloc", st)
+
+
 def kl_backward(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, logp: torch.Tensor,
                 lse: torch.Tensor, grad: torch.Tensor, chunk: int, need_dH: bool = True,
                 need_dW: bool = True, dW_out: Optional[torch.Tensor] = None,

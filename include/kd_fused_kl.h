@@ -186,6 +186,39 @@ int kd_fused_kl_bwd_ex(const void* H, const void* W, int dtype, const int32_t* t
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The forward pass without a workspace and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, and harnesses that forbid allocation.
+ *
+ * Arguments, results and errors are those of kd_fused_kl_fwd_ex with the
+ * workspace left out. The scratch the forward needs (the bucketed cache of a
+ * group of chunks, the transposed chunk of H, the tile partials, and the
+ * per-position losses when loss_tok is NULL) lives instead in a device array
+ * held by the library: KD_NOALLOC_SCRATCH_BYTES bytes on every GPU the
+ * library runs on, kept until the process ends. Sizes whose forward
+ * workspace, kd_fused_kl_workspace_bytes(KD_PASS_FWD, ...), exceeds it are
+ * rejected with KD_ERR_WORKSPACE before anything is enqueued. 64 MiB holds
+ * the forward of the 8K-token head (17 MiB), of 32,768 tokens at d = 3072,
+ * V = 128,256, K = 100, chunk 2048 (46 MiB) and of the 201,088-token head at
+ * the same N (50 MiB); from 65,536 tokens at K = 100 the bucketed cache alone
+ * takes 52 MiB and the call is rejected. The stream must belong to the
+ * current device (KD_ERR_INVALID_ARG otherwise).
+ *
+ * The first call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress); make it once outside graph capture. No call
+ * allocates or frees device memory or calls hipMemset; the scratch is
+ * cleared by fill kernels. Every call on a GPU shares that GPU's array: calls
+ * that overlap on one GPU (two streams, or two host threads) race and give
+ * undefined results. Kernel timing (kd_timing_enable) is not recorded for
+ * this call, since recording it would create events.
+ */
+#define KD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int kd_fused_kl_fwd_noalloc(const void* H, const void* W, int dtype, const int32_t* topk_idx,
+                            const float* topk_logp, const float* weight, int reduction,
+                            int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk,
+                            float* loss_tok, float* lse, float* loss, void* stream);
+
+/*
  * Loss and gradients in one call, for callers that know the upstream
  * gradient g when they compute the loss (g = 1 for a loss that is the
  * objective, or a fixed scale).

@@ -341,7 +341,7 @@ int main(void) {
   const fn_t fns[] = {
       (fn_t)kd_status_str, (fn_t)kd_fused_kl_workspace_bytes,
       (fn_t)kd_fused_kl_fwd, (fn_t)kd_fused_kl_bwd,
-      (fn_t)kd_fused_kl_fwd_ex, (fn_t)kd_fused_kl_bwd_ex,
+      (fn_t)kd_fused_kl_fwd_ex, (fn_t)kd_fused_kl_bwd_ex, (fn_t)kd_fused_kl_fwd_noalloc,
       (fn_t)kd_fused_kl_fwd_bwd, (fn_t)kd_teacher_topk,
       (fn_t)kd_fused_kl_check_inputs, (fn_t)kd_cast_f32_to_bf16, (fn_t)kd_scale,
       (fn_t)kd_timing_enable, (fn_t)kd_timing_read};
