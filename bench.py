@@ -559,13 +559,38 @@ def run_gemm_ceiling(steps, warmup, dev):
     }), flush=True)
 
 
+def run_hbm_copy(steps, warmup, dev):
+    """A plain 1 GiB device-to-device copy (torch copy_ of 256 Mi float32):
+    the HBM bandwidth one copy kernel reaches, and the reference a counter
+    profile of it gives for scaling FETCH_SIZE and WRITE_SIZE to bytes (it
+    reads and writes exactly 1 GiB per call)."""
+    import torch
+
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(max(warmup, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"what": "device copy of 1 GiB (reads 1 GiB, writes 1 GiB)", "bytes_read": 4 * n,
+                      "bytes_written": 4 * n, "ms": ms, "GB_per_s": 2 * 4 * n / ms / 1e6,
+                      "steps": steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="8k-head",
-                    choices=[*WORKLOADS, "sweep", "teacher-cache", "gemm-ceiling"])
+                    choices=[*WORKLOADS, "sweep", "teacher-cache", "gemm-ceiling", "hbm-copy"])
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -612,6 +637,9 @@ def main():
         return
     if args.workload == "gemm-ceiling":
         run_gemm_ceiling(args.steps, args.warmup, dev)
+        return
+    if args.workload == "hbm-copy":
+        run_hbm_copy(args.steps, args.warmup, dev)
         return
 
     cid, _ = WORKLOADS[args.workload]

@@ -236,29 +236,63 @@ __global__ __launch_bounds__(256) void k_prep_count(const int* __restrict__ idx,
   if (lane == 0) rowS[row] = s;
 }
 
-// Exclusive scan of the bucket counts (one workgroup).
+// Exclusive scan of the bucket counts (one workgroup). The counts pass
+// through LDS in tiles of 1024·kScanE: loaded and stored coalesced, each
+// thread scans kScanE consecutive counts, the threads' sums are scanned by
+// wave shuffles and the sixteen wave totals, and a running carry links the
+// tiles.
+constexpr int kScanE = 8;
 __global__ __launch_bounds__(1024) void k_prep_scan(const int* __restrict__ counts,
                                                     int* __restrict__ offsets, int nb) {
-  __shared__ int sh[1024];
-  const int t = threadIdx.x;
-  const int per = (nb + 1023) / 1024;
-  const int b = t * per, e = b + per < nb ? b + per : nb;
-  int s = 0;
-  for (int i = b; i < e; ++i) s += counts[i];
-  sh[t] = s;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = t >= off ? sh[t - off] : 0;
+  constexpr int kTile = 1024 * kScanE;
+  __shared__ int tile[kTile];
+  __shared__ int wsum[16];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int carry = 0;
+  for (int base = 0; base < nb; base += kTile) {
+#pragma unroll
+    for (int e = 0; e < kScanE; ++e) {
+      const int i = base + e * 1024 + t;
+      tile[e * 1024 + t] = i < nb ? counts[i] : 0;
+    }
     __syncthreads();
-    sh[t] += v;
+    int v[kScanE];
+    int sum = 0;
+#pragma unroll
+    for (int e = 0; e < kScanE; ++e) {
+      v[e] = tile[t * kScanE + e];
+      sum += v[e];
+    }
+    int incl = sum;  // inclusive scan of the threads' sums within the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wsum[w] = incl;
     __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      before += j < w ? wsum[j] : 0;
+      total += wsum[j];
+    }
+    int run = carry + before + incl - sum;
+#pragma unroll
+    for (int e = 0; e < kScanE; ++e) {
+      tile[t * kScanE + e] = run;
+      run += v[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kScanE; ++e) {
+      const int i = base + e * 1024 + t;
+      if (i < nb) offsets[i] = tile[e * 1024 + t];
+    }
+    carry += total;
+    __syncthreads();  // the tile and wsum are reused by the next round
   }
-  int base = sh[t] - s;
-  for (int i = b; i < e; ++i) {
-    offsets[i] = base;
-    base += counts[i];
-  }
-  if (t == 1023) offsets[nb] = sh[1023];
+  if (t == 0) offsets[nb] = carry;
 }
 
 // Scatter hit records into their buckets. Counting down leaves `counts` at

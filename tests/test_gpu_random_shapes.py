@@ -7,6 +7,9 @@ upstream gradient, and (half the time) per-position weights with the sum or
 the mean. Inputs follow the workloads' recipe (test_gpu_parity._case). Both
 the two-pass calls and the one-pass call are compared with the fp64 oracle
 at the tolerances of test_gpu_parity.py, and with each other bit for bit.
+A second set draws bf16 shapes with d in [264, 1048], not a multiple of 256,
+so the dH and dW launches hold full d tiles and a ragged last one read
+through the transposing bf16 loads at a nonzero column base.
 """
 import numpy as np
 import pytest
@@ -33,9 +36,33 @@ def _shape(i):
     return N, d, V, K, dtype, chunk, grad, weighted, reduction
 
 
+def _wide_shape(i):
+    r = np.random.default_rng(9500 + i)
+    N = int(r.integers(1, 601))
+    d = int(r.integers(33, 132)) * 8
+    if d % 256 == 0:
+        d += 8
+    V = int(r.integers(2, 3001))
+    K = int(r.integers(1, min(V, 128) + 1))
+    chunk = int(r.integers(1, 601))
+    grad = float(r.uniform(0.2, 2.0))
+    weighted = bool(r.random() < 0.5)
+    reduction = "mean" if (weighted and r.random() < 0.5) else "sum"
+    return N, d, V, K, "bf16", chunk, grad, weighted, reduction
+
+
 @pytest.mark.parametrize("i", range(24))
 def test_random_shape(kd, i):
-    N, d, V, K, dtype, chunk, grad, weighted, red = _shape(i)
+    _check(kd, i, _shape(i))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_wide_bf16_shape(kd, i):
+    _check(kd, 100 + i, _wide_shape(i))
+
+
+def _check(kd, i, shape):
+    N, d, V, K, dtype, chunk, grad, weighted, red = shape
     what = f"case {i}: N={N} d={d} V={V} K={K} {dtype} chunk={chunk} {red} w={weighted}"
     print(what, flush=True)
     H, W, idx, logp = _case(N, d, V, K, dtype, seed=i)
