@@ -119,6 +119,8 @@ def test_chunk_size_does_not_change_results(kd, chunk):
     (300, 64, 20000, 16383, "f32", 128), # the largest K (the hit record's 14-bit field), 82% of V cached
     (260, 320, 1100, 9, "bf16", 128),    # d = 320: one full 256-wide d tile and a 64-wide one
     (300, 2880, 1500, 20, "bf16", 128),  # d = 2880 (the gpt-oss head): 11 full d tiles + 64 columns
+    (150, 1800, 700, 10, "bf16", 64),    # 8 d tiles: dW's groups of six d tiles and a group of two
+    (130, 3336, 520, 7, "bf16", 128),    # 14 d tiles: two groups of six, a group of two, 8-column last tile
 ])
 def test_edge_shapes(kd, N, d, V, K, dtype, chunk):
     H, W, idx, logp = _case(N, d, V, K, dtype, seed=N * 7 + V)
