@@ -488,10 +488,11 @@ def run_gemm_ceiling(steps, warmup, dev):
     torch.cuda.synchronize()
 
     def mm_f32(a, b):
-        try:
-            return torch.mm(a, b, out_dtype=torch.float32)
-        except (TypeError, RuntimeError):
-            return torch.mm(a, b)
+        # bf16 operands, float32 output (torch's out_dtype form of mm)
+        return torch.mm(a, b, out_dtype=torch.float32)
+
+    if mm_f32(dlT[:256], Hw).dtype != torch.float32:
+        raise RuntimeError("torch.mm did not produce a float32 output for the dW case")
 
     cases = {
         "logits (H_c . W^T)": (lambda: torch.mm(Hc, W.t()), 2.0 * C * cfg.d * cfg.V),
