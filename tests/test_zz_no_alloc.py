@@ -98,3 +98,19 @@ def test_noalloc_rejects_sizes_beyond_its_scratch(kd):
     kd.kl_forward_noalloc(H[:n2], W, idx[:n2], logp[:n2], chunk, loss, lse[:n2])
     torch.cuda.synchronize()
     assert np.isfinite(loss.item())
+
+
+def test_noalloc_at_the_8k_head(kd):
+    """The 8K-token head in the bench's launch configuration (17 MiB of the
+    64 MiB scratch): bitwise the workspace forward's outputs."""
+    import workload
+
+    cfg = workload.config(3)
+    H, W, idx, logp = workload.make_inputs(cfg, teacher_device="cuda")
+    Hd, Wd, id_, lp = _to_dev(H, W, idx, logp)
+    l2, t2, s2 = _noalloc(kd, Hd, Wd, id_, lp, cfg.chunk)
+    l1, t1, s1 = kd.kl_forward(Hd, Wd, id_, lp, cfg.chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(l1, l2) and torch.equal(t1, t2) and torch.equal(s1, s2)
+    del Hd, Wd, id_, lp
+    torch.cuda.empty_cache()
