@@ -653,8 +653,9 @@ def main():
     ks = r["kernels"]
     gemms = ["fwd_logits", "bwd_dlogits", "bwd_dh", "bwd_dw"]
     dom = max(gemms, key=lambda k: ks[k]["total_ms"])
-    # Each of the four contractions does 2·rows·d·V flops per launch (one
-    # launch per chunk), so over the timed steps it did 2·N·d·V·steps.
+    # Each of the four contractions does 2·rows·d·V flops for the rows a
+    # launch covers (a group of chunks, a dW window), so over the timed steps
+    # it did 2·N·d·V·steps.
     dom_ms = ks[dom]["total_ms"]
     achieved = 2.0 * N * d * V * args.steps / (dom_ms / 1e3) / 1e12 if dom_ms > 0 else 0.0
     kernels_out = {k: {"avg_ms": (v["total_ms"] / v["launches"]) if v["launches"] else 0.0,

@@ -120,15 +120,22 @@ __global__ void k_cast_f32_bf16(const float* __restrict__ src, __bf16* __restric
     dst[i] = __bf16(src[i]);
 }
 
-// dst[c][r] = src[r][c] for a [rows][cols] matrix of 16-bit elements (a bf16
-// chunk of H into the [d][tokens] layout the logit GEMM streams as a column
-// operand). dst rows are written for r < rows_pad, zero from `rows` on.
-// Needs cols % 8 == 0, rows_pad % 8 == 0 and 16-byte aligned rows.
+// dst[c][r] = src[r][c] for a [rows][cols] matrix of 16-bit elements (bf16
+// chunks of H into the [d][tokens] layout the logit GEMM streams as a column
+// operand), one chunk of C source rows per blockIdx.z: chunk z is rows
+// z·C .. min(rows, (z+1)·C) − 1 of src, and becomes its own [cols][rows_pad]
+// block at dst + z·dst_chunk. Block rows are written for r < rows_pad, zero
+// past the chunk's rows. Needs cols % 8 == 0, rows_pad % 8 == 0 and 16-byte
+// aligned rows.
 __global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict__ src,
                                                      int64_t ld_src, int rows, int cols,
                                                      uint16_t* __restrict__ dst, int64_t ld_dst,
-                                                     int rows_pad) {
+                                                     int rows_pad, int C, int64_t dst_chunk) {
   __shared__ uint16_t t[64][66];
+  const int z = blockIdx.z;
+  src += int64_t(z) * C * ld_src;
+  dst += int64_t(z) * dst_chunk;
+  rows = rows - z * C < C ? rows - z * C : C;
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64, tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -326,20 +333,63 @@ __global__ __launch_bounds__(256) void k_prep_scatter(const int* __restrict__ id
 // N, from the chunk of H). Each lane holds, for one token column per block,
 // 64 vocabulary values; a token's (max, Σexp) over the tile needs one
 // cross-half shuffle and one exchange between the two waves sharing it.
+//
+// A launch covers nch consecutive chunks of C rows (`rows` in all; only the
+// last chunk may be shorter). Its tiles run chunk by chunk, and inside a
+// chunk vocabulary-tile major, token tile fastest. Each chunk's operands and
+// buffers follow the previous chunk's at fixed strides, so the kernel forms
+// the chunk's own view (ChunkView) and works on that.
 struct FwdArgs {
   RowOp W;   // [V][d]
-  RowOp H;   // chunk rows of H, [rows][d] (float32 path)
-  ColOp Ht;  // the same chunk transposed, [d][C_pad] (bf16 path)
+  RowOp H;   // rows of H from the first chunk's first, [.][d] (float32 path)
+  ColOp Ht;  // the first chunk transposed, [d][C_pad] (bf16 path)
   int kt;   // stages along d
-  int tiles_t, tiles_v;
+  int tiles_t, tiles_v;  // token tiles of all the launch's chunks; vocabulary tiles
+  int nch, C, nMt, nb;   // chunks, rows per chunk, token tiles and buckets per full chunk
+  int64_t ht_chunk;      // bytes from one chunk's transposed block to the next
   int rows, V, K, nVt;
-  const int* offsets;
+  const int* offsets;  // bucket offsets of the first chunk, nb per chunk
   const uint2* recs;
-  float* zhit;     // [C, K]: z at the cached ids
-  float2* part;    // [C_pad, nVt]: (max, Σexp) of each token over each vocabulary tile
-  float* z;        // STORE_Z: the chunk's logits, [rows][ld_z] float32, token-major
+  float* zhit;     // [rows, K]: z at the cached ids
+  float2* part;    // [rows, nVt]: (max, Σexp) of each token over each vocabulary tile
+  float* z;        // STORE_Z (one chunk only): the chunk's logits, [rows][ld_z] float32
   int64_t ld_z;
 };
+
+// Chunk and tile of a logical workgroup index, in the order above.
+struct ChunkView {
+  int c;       // chunk within the launch
+  int rows;    // its rows
+  int tt, vt;  // token and vocabulary tile within the chunk
+};
+
+__device__ __forceinline__ ChunkView chunk_view(int logical, int nch, int C, int nMt, int rows,
+                                                int tiles_v) {
+  ChunkView v;
+  const int per = nMt * tiles_v;  // tiles of a full chunk
+  v.c = logical / per;
+  const int rem = logical - v.c * per;
+  const int left = rows - v.c * C;
+  v.rows = left < C ? left : C;
+  const int tc = v.c + 1 < nch ? nMt : (v.rows + kBN - 1) / kBN;
+  v.tt = rem % tc;
+  v.vt = rem / tc;
+  return v;
+}
+
+// The launch's arguments narrowed to the chunk of `v`.
+__device__ __forceinline__ FwdArgs narrow(const FwdArgs& a, const ChunkView& v) {
+  FwdArgs n = a;
+  n.H.base += int64_t(v.c) * a.C * a.H.ld;
+  n.H.rows = v.rows;
+  n.Ht.base += int64_t(v.c) * a.ht_chunk;
+  n.Ht.cbytes = v.rows * 2;
+  n.rows = v.rows;
+  if (a.offsets) n.offsets += int64_t(v.c) * a.nb;
+  if (a.zhit) n.zhit += int64_t(v.c) * a.C * a.K;
+  n.part += int64_t(v.c) * a.C * a.nVt;
+  return n;
+}
 
 // Hit records of one tile. The epilogue starts by loading the first 64
 // records (one coalesced 8-byte load per lane) so their latency overlaps the
@@ -459,12 +509,14 @@ __device__ __forceinline__ void gather_hit_logits(const Acc& acc, lds_f32* regio
 // writes the whole tile of logits (float32, token-major), and the cached ids
 // are read back from there per row.
 template <bool BF16, bool STORE_Z>
-__global__ __launch_bounds__(kThreads) void k_fwd_logits(FwdArgs a) {
+__global__ __launch_bounds__(kThreads) void k_fwd_logits(FwdArgs args) {
   __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
   lds_t* smem = (lds_t*)(smem_raw);
-  const int nblk = a.tiles_t * a.tiles_v;
+  const int nblk = args.tiles_t * args.tiles_v;
   const int logical = xcd_logical(blockIdx.x, nblk);
-  const int tt = logical % a.tiles_t, vt = logical / a.tiles_t;
+  const ChunkView cv = chunk_view(logical, args.nch, args.C, args.nMt, args.rows, args.tiles_v);
+  const FwdArgs a = narrow(args, cv);
+  const int tt = cv.tt, vt = cv.vt;
   const int t_base = tt * kBN, v_base = vt * kBM;
 
   Acc acc;
@@ -677,31 +729,55 @@ __global__ __launch_bounds__(256) void k_dl_hits(const float* __restrict__ z, in
 // --------------------------------------------------------------------------
 // backward: recompute the logit tile and turn it into dlogits in registers
 // --------------------------------------------------------------------------
+// A launch covers the chunks of one dW window, laid out and walked as in the
+// forward (FwdArgs).
 struct DlArgs {
   RowOp W;
-  RowOp H;   // float32 path
-  ColOp Ht;  // bf16 path: the chunk transposed, [d][C_pad]
+  RowOp H;   // float32 path: rows of H from the first chunk's first
+  ColOp Ht;  // bf16 path: the first chunk transposed, [d][C_pad]
   int kt;
-  int tiles_t, tiles_v;
+  int tiles_t, tiles_v;  // token tiles of all the launch's chunks; vocabulary tiles
+  int nch, C, nMt, nb;   // chunks, rows per chunk, token tiles and buckets per full chunk
+  int64_t ht_chunk;      // bytes from one chunk's transposed block to the next
   int rows, V, nVt;
-  const int* offsets;
+  const int* offsets;  // bucket offsets of the first chunk, nb per chunk
   const uint2* recs;
-  const float* lse;   // chunk's lse (forward output)
-  const float* rowS;  // chunk's S_r
+  const float* lse;   // the rows' lse (forward output)
+  const float* rowS;  // the rows' S_r
   const float* grad;  // device scalar: g, or g / Σw for the mean
-  const float* w;     // chunk's per-token weights, or nullptr (all 1)
-  void* dl;           // [C_pad, V_pad] of the compute dtype, token-major
+  const float* w;     // the rows' per-token weights, or nullptr (all 1)
+  void* dl;           // [rows, V_pad] of the compute dtype, token-major
   int64_t ld_dl;      // elements
 };
 
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs a) {
+__device__ __forceinline__ DlArgs narrow(const DlArgs& a, const ChunkView& v) {
+  typedef typename Elt<BF16>::T T;
+  DlArgs n = a;
+  const int64_t r0 = int64_t(v.c) * a.C;
+  n.H.base += r0 * a.H.ld;
+  n.H.rows = v.rows;
+  n.Ht.base += int64_t(v.c) * a.ht_chunk;
+  n.Ht.cbytes = v.rows * 2;
+  n.rows = v.rows;
+  n.offsets += int64_t(v.c) * a.nb;
+  n.lse += r0;
+  n.rowS += r0;
+  if (a.w) n.w += r0;
+  n.dl = static_cast<T*>(a.dl) + r0 * a.ld_dl;
+  return n;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs args) {
   typedef typename Elt<BF16>::T T;
   __shared__ __attribute__((aligned(16))) char smem_raw[kSmemBytes];
   lds_t* smem = (lds_t*)(smem_raw);
-  const int nblk = a.tiles_t * a.tiles_v;
+  const int nblk = args.tiles_t * args.tiles_v;
   const int logical = xcd_logical(blockIdx.x, nblk);
-  const int tt = logical % a.tiles_t, vt = logical / a.tiles_t;
+  const ChunkView cv = chunk_view(logical, args.nch, args.C, args.nMt, args.rows, args.tiles_v);
+  const DlArgs a = narrow<BF16>(args, cv);
+  const int tt = cv.tt, vt = cv.vt;
   const int t_base = tt * kBN, v_base = vt * kBM;
 
   Acc acc;
@@ -1384,16 +1460,43 @@ void launch_prep(const Plan& p, const Ws& ws, const int32_t* idx, const float* l
 // Bucket offsets and S_r of the chunk in slot `slot` of the current group.
 inline int64_t prep_slot(const Plan& p, int64_t r0) { return (r0 / p.C) % p.prep_chunks; }
 
-// The bf16 logit GEMMs stream the chunk of H as a column operand: transpose
-// it into [d][C_pad] once per chunk and pass that layout.
-ColOp chunk_transposed(const Plan& p, const Ws& ws, const char* Hc, int rows, hipStream_t st) {
+// The bf16 logit GEMMs stream each chunk of H as a column operand: the
+// launch's chunks (`rows` rows from Hc on) are transposed, each into its own
+// [d][C_pad] block, in one launch before the GEMM. Returns the first block.
+ColOp chunks_transposed(const Plan& p, const Ws& ws, const char* Hc, int rows, hipStream_t st) {
   uint16_t* ht = ws.at<uint16_t>(p.off_ht);
+  const int nch = int(cdiv(rows, p.C));
   timed(KD_KERNEL_PREP, st, [&] {
-    hipLaunchKernelGGL(k_transpose16, dim3(cdiv(p.C_pad, 64), cdiv(p.d, 64)), dim3(256), 0, st,
-                       reinterpret_cast<const uint16_t*>(Hc), p.d, rows, int(p.d), ht, p.C_pad,
-                       int(p.C_pad));
+    hipLaunchKernelGGL(k_transpose16, dim3(cdiv(p.C_pad, 64), cdiv(p.d, 64), nch), dim3(256), 0,
+                       st, reinterpret_cast<const uint16_t*>(Hc), p.d, rows, int(p.d), ht,
+                       p.C_pad, int(p.C_pad), int(p.C), p.d * p.C_pad);
   });
-  return ColOp{reinterpret_cast<const char*>(ht), p.C_pad * 2, int(p.d), rows * 2};
+  const int first = rows < p.C ? rows : int(p.C);
+  return ColOp{reinterpret_cast<const char*>(ht), p.C_pad * 2, int(p.d), first * 2};
+}
+
+// The chunk-group fields shared by FwdArgs and DlArgs, for a launch over the
+// chunks holding rows r0 .. r0 + rows − 1 (whole chunks but the last).
+template <class Args>
+void set_chunk_group(Args& a, const Plan& p, const void* H, const void* W, int64_t r0, int rows,
+                     const ColOp& Ht) {
+  const int64_t row_bytes = p.d * p.es;
+  const int nch = int(cdiv(rows, p.C));
+  a.W = RowOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
+  a.H = RowOp{static_cast<const char*>(H) + r0 * row_bytes, row_bytes,
+              rows < p.C ? rows : int(p.C), int(row_bytes)};
+  a.Ht = Ht;
+  a.kt = int(p.kt_d);
+  a.nch = nch;
+  a.C = int(p.C);
+  a.nMt = int(p.nMt);
+  a.nb = int(p.nb);
+  a.ht_chunk = p.d * p.C_pad * 2;
+  a.tiles_t = int((nch - 1) * p.nMt + cdiv(rows - int64_t(nch - 1) * p.C, kBN));
+  a.tiles_v = int(p.nVt);
+  a.rows = rows;
+  a.V = int(p.V);
+  a.nVt = int(p.nVt);
 }
 
 void launch_reset(const Plan& p, const Ws& ws, hipStream_t st) {
@@ -1414,22 +1517,17 @@ int run_fwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
   if (p.N > 0) {
     launch_reset(p, ws, st);
     const int64_t row_bytes = p.d * p.es;
-    for (int64_t r0 = 0; r0 < p.N; r0 += p.C) {
-      const int rows = int(p.N - r0 < p.C ? p.N - r0 : p.C);
+    const int64_t span = p.fwd_group * p.C;  // rows of one logit launch
+    for (int64_t r0 = 0; r0 < p.N; r0 += span) {
+      const int rows = int(p.N - r0 < span ? p.N - r0 : span);
       const int64_t slot = prep_slot(p, r0);
       if (slot == 0) launch_prep(p, ws, idx, logp, r0, st);
       FwdArgs a;
-      a.W = RowOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
-      a.H = RowOp{static_cast<const char*>(H) + r0 * row_bytes, row_bytes, rows, int(row_bytes)};
-      a.Ht = BF16 ? chunk_transposed(p, ws, static_cast<const char*>(H) + r0 * row_bytes, rows, st)
-                  : ColOp{};
-      a.kt = int(p.kt_d);
-      a.tiles_t = int(cdiv(rows, kBN));
-      a.tiles_v = int(p.nVt);
-      a.rows = rows;
-      a.V = int(p.V);
+      set_chunk_group(a, p, H, W, r0, rows,
+                      BF16 ? chunks_transposed(p, ws, static_cast<const char*>(H) + r0 * row_bytes,
+                                               rows, st)
+                           : ColOp{});
       a.K = int(p.K);
-      a.nVt = int(p.nVt);
       a.offsets = ws.at<int>(p.off_offsets) + slot * p.nb;
       a.recs = ws.at<uint2>(p.off_recs);
       a.zhit = ws.at<float>(p.off_zhit);
@@ -1523,48 +1621,32 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
   float* const gscale = ws.at<float>(p.off_gscale);
   hipLaunchKernelGGL(k_grad_scale, dim3(1), dim3(1024), 0, st, grad, weight, p.N, mean, gscale);
   const int64_t row_bytes = p.d * p.es;
-  const int64_t dl_ld_bytes = p.V_pad * p.es;
-  int64_t win_r0 = 0;   // first row of the current dW window
-  int win_chunks = 0;   // chunks of the window held in the dlogits scratch
+  const int64_t span = int64_t(p.dw_window) * p.C;  // rows of one dW window
   bool dw_written = accumulate != 0;
-  for (int64_t r0 = 0; r0 < p.N; r0 += p.C) {
-    const int rows = int(p.N - r0 < p.C ? p.N - r0 : p.C);
+  for (int64_t r0 = 0; r0 < p.N; r0 += span) {
+    const int rows = int(p.N - r0 < span ? p.N - r0 : span);
     const int64_t slot = prep_slot(p, r0);
     if (slot == 0) launch_prep(p, ws, idx, logp, r0, st);
-    const char* Hc = static_cast<const char*>(H) + r0 * row_bytes;
-    const int tiles_t = int(cdiv(rows, kBN));
-    if (win_chunks == 0) win_r0 = r0;
-    char* const dl_c = ws.at<char>(p.off_dl) + int64_t(win_chunks) * p.C * dl_ld_bytes;
-
+    // The window's dlogits, all its chunks in one launch, into the scratch
+    // ([rows][V_pad], the chunks back to back).
     DlArgs a;
-    a.W = RowOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
-    a.H = RowOp{Hc, row_bytes, rows, int(row_bytes)};
-    a.Ht = BF16 ? chunk_transposed(p, ws, Hc, rows, st) : ColOp{};
-    a.kt = int(p.kt_d);
-    a.tiles_t = tiles_t;
-    a.tiles_v = int(p.nVt);
-    a.rows = rows;
-    a.V = int(p.V);
-    a.nVt = int(p.nVt);
+    set_chunk_group(a, p, H, W, r0, rows,
+                    BF16 ? chunks_transposed(p, ws, static_cast<const char*>(H) + r0 * row_bytes,
+                                             rows, st)
+                         : ColOp{});
     a.offsets = ws.at<int>(p.off_offsets) + slot * p.nb;
     a.recs = ws.at<uint2>(p.off_recs);
     a.lse = lse + r0;
     a.rowS = ws.at<float>(p.off_rowS) + slot * p.C;
     a.grad = gscale;
     a.w = weight ? weight + r0 : nullptr;
-    a.dl = dl_c;
+    a.dl = ws.at<char>(p.off_dl);
     a.ld_dl = p.V_pad;
     timed(KD_KERNEL_BWD_DLOGITS, st, [&] {
       hipLaunchKernelGGL(k_bwd_dlogits<BF16>, dim3(a.tiles_t * a.tiles_v), dim3(kThreads), 0, st,
                          a);
     });
-
-    ++win_chunks;
-    const bool last = r0 + rows >= p.N;
-    if (win_chunks == p.dw_window || last) {
-      launch_window<BF16>(p, ws, H, W, win_r0, int(r0 + rows - win_r0), dH, dW, dw_written, st);
-      win_chunks = 0;
-    }
+    launch_window<BF16>(p, ws, H, W, r0, rows, dH, dW, dw_written, st);
   }
   return launch_status();
 }
@@ -1604,16 +1686,8 @@ int run_fwd_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx,
     char* const dl_c = ws.at<char>(p.off_dl) + int64_t(win_chunks) * p.C * dl_ld_bytes;
 
     FwdArgs a;
-    a.W = RowOp{static_cast<const char*>(W), row_bytes, int(p.V), int(row_bytes)};
-    a.H = RowOp{Hc, row_bytes, rows, int(row_bytes)};
-    a.Ht = BF16 ? chunk_transposed(p, ws, Hc, rows, st) : ColOp{};
-    a.kt = int(p.kt_d);
-    a.tiles_t = int(cdiv(rows, kBN));
-    a.tiles_v = int(p.nVt);
-    a.rows = rows;
-    a.V = int(p.V);
+    set_chunk_group(a, p, H, W, r0, rows, BF16 ? chunks_transposed(p, ws, Hc, rows, st) : ColOp{});
     a.K = int(p.K);
-    a.nVt = int(p.nVt);
     a.offsets = nullptr;
     a.recs = nullptr;
     a.zhit = nullptr;
@@ -1664,16 +1738,8 @@ int run_teacher(const Plan& p, const void* Ht, const void* Wt, int32_t* idx, flo
     const int rows = int(p.N - r0 < p.C ? p.N - r0 : p.C);
     const char* Hc = static_cast<const char*>(Ht) + r0 * row_bytes;
     FwdArgs a;
-    a.W = RowOp{static_cast<const char*>(Wt), row_bytes, int(p.V), int(row_bytes)};
-    a.H = RowOp{Hc, row_bytes, rows, int(row_bytes)};
-    a.Ht = BF16 ? chunk_transposed(p, ws, Hc, rows, st) : ColOp{};
-    a.kt = int(p.kt_d);
-    a.tiles_t = int(cdiv(rows, kBN));
-    a.tiles_v = int(p.nVt);
-    a.rows = rows;
-    a.V = int(p.V);
+    set_chunk_group(a, p, Ht, Wt, r0, rows, BF16 ? chunks_transposed(p, ws, Hc, rows, st) : ColOp{});
     a.K = int(p.K);
-    a.nVt = int(p.nVt);
     a.offsets = nullptr;  // there are no cached ids
     a.recs = nullptr;
     a.zhit = nullptr;
@@ -1736,6 +1802,28 @@ struct NoEventsScope {
   ~NoEventsScope() { t_no_events = false; }
 };
 
+// The forward call's argument checks and launches, for a plan of its shape.
+int fwd_with_plan(const Plan& p, const void* H, const void* W, int dtype, const int32_t* topk_idx,
+                  const float* topk_logp, const float* weight, int reduction, float* loss_tok,
+                  float* lse, float* loss, void* workspace, size_t workspace_bytes, void* stream) {
+  if (reduction != KD_REDUCE_SUM && reduction != KD_REDUCE_MEAN) return KD_ERR_INVALID_ARG;
+  if (loss == nullptr || !aligned(loss, 4)) return KD_ERR_INVALID_ARG;
+  if (p.N > 0) {
+    if (!H || !W || !topk_idx || !topk_logp || !lse) return KD_ERR_INVALID_ARG;
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(topk_idx, 4) || !aligned(topk_logp, 4) ||
+        !aligned(lse, 4) || (loss_tok && !aligned(loss_tok, 4)) || (weight && !aligned(weight, 4)))
+      return KD_ERR_INVALID_ARG;
+  }
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.total) return KD_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float* w = p.N > 0 ? weight : nullptr;
+  const int mean = reduction == KD_REDUCE_MEAN;
+  return dtype == KD_BF16 ? run_fwd<true>(p, H, W, topk_idx, topk_logp, w, mean, loss_tok, lse,
+                                          loss, workspace, s)
+                          : run_fwd<false>(p, H, W, topk_idx, topk_logp, w, mean, loss_tok, lse,
+                                           loss, workspace, s);
+}
+
 }  // namespace
 }  // namespace kd
 
@@ -1769,24 +1857,8 @@ int kd_fused_kl_fwd_ex(const void* H, const void* W, int dtype, const int32_t* t
   kd::Plan p;
   const int st = kd::make_plan(KD_PASS_FWD, N, d, V, K, chunk, dtype, &p);
   if (st != KD_OK) return st;
-  if (reduction != KD_REDUCE_SUM && reduction != KD_REDUCE_MEAN) return KD_ERR_INVALID_ARG;
-  if (loss == nullptr || !kd::aligned(loss, 4)) return KD_ERR_INVALID_ARG;
-  if (N > 0) {
-    if (!H || !W || !topk_idx || !topk_logp || !lse) return KD_ERR_INVALID_ARG;
-    if (!kd::aligned(H, 16) || !kd::aligned(W, 16) || !kd::aligned(topk_idx, 4) ||
-        !kd::aligned(topk_logp, 4) || !kd::aligned(lse, 4) ||
-        (loss_tok && !kd::aligned(loss_tok, 4)) || (weight && !kd::aligned(weight, 4)))
-      return KD_ERR_INVALID_ARG;
-  }
-  if (!workspace || !kd::aligned(workspace, 256) || workspace_bytes < p.total)
-    return KD_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const float* w = N > 0 ? weight : nullptr;
-  const int mean = reduction == KD_REDUCE_MEAN;
-  return dtype == KD_BF16 ? kd::run_fwd<true>(p, H, W, topk_idx, topk_logp, w, mean, loss_tok, lse,
-                                              loss, workspace, s)
-                          : kd::run_fwd<false>(p, H, W, topk_idx, topk_logp, w, mean, loss_tok, lse,
-                                               loss, workspace, s);
+  return kd::fwd_with_plan(p, H, W, dtype, topk_idx, topk_logp, weight, reduction, loss_tok, lse,
+                           loss, workspace, workspace_bytes, stream);
 }
 
 int kd_fused_kl_fwd_noalloc(const void* H, const void* W, int dtype, const int32_t* topk_idx,
@@ -1794,9 +1866,15 @@ int kd_fused_kl_fwd_noalloc(const void* H, const void* W, int dtype, const int32
                             int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk,
                             float* loss_tok, float* lse, float* loss, void* stream) {
   kd::Plan p;
-  const int st = kd::make_plan(KD_PASS_FWD, N, d, V, K, chunk, dtype, &p);
+  int st = kd::make_plan(KD_PASS_FWD, N, d, V, K, chunk, dtype, &p);
   if (st != KD_OK) return st;
-  if (p.total > KD_NOALLOC_SCRATCH_BYTES) return KD_ERR_WORKSPACE;
+  // Past the scratch, one chunk per logit launch: the same results from a
+  // smaller workspace.
+  if (p.total > KD_NOALLOC_SCRATCH_BYTES) {
+    st = kd::make_plan(KD_PASS_FWD, N, d, V, K, chunk, dtype, &p, 0);
+    if (st != KD_OK) return st;
+    if (p.total > KD_NOALLOC_SCRATCH_BYTES) return KD_ERR_WORKSPACE;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess) return KD_ERR_HIP;
@@ -1809,8 +1887,8 @@ int kd_fused_kl_fwd_noalloc(const void* H, const void* W, int dtype, const int32
   const int got = kd::scratch_on_current_device(&ws);
   if (got != KD_OK) return got;
   kd::NoEventsScope no_events;
-  return kd_fused_kl_fwd_ex(H, W, dtype, topk_idx, topk_logp, weight, reduction, N, d, V, K, chunk,
-                            loss_tok, lse, loss, ws, KD_NOALLOC_SCRATCH_BYTES, stream);
+  return kd::fwd_with_plan(p, H, W, dtype, topk_idx, topk_logp, weight, reduction, loss_tok, lse,
+                           loss, ws, KD_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int kd_fused_kl_fwd(const void* H, const void* W, int dtype, const int32_t* topk_idx,

@@ -12,7 +12,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 }  // namespace
 
 int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, int dtype,
-              Plan* p) {
+              Plan* p, int64_t fwd_group_rows) {
   if (p == nullptr) return KD_ERR_INVALID_ARG;
   if (pass != KD_PASS_FWD && pass != KD_PASS_BWD && pass != KD_PASS_TEACHER &&
       pass != KD_PASS_FWD_BWD)
@@ -56,11 +56,35 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
     return KD_ERR_UNSUPPORTED;
 
   const int64_t n_chunks = N > 0 ? cdiv(N, q.C) : 1;
+  // The prep group: chunks whose cached entries one prep pass buckets.
+  int64_t group = kPrepBuckets / q.nb;
+  if (group > kPrepRows / q.C) group = kPrepRows / q.C;
+  if (group > n_chunks) group = n_chunks;
+  if (group < 1) group = 1;
+  // The backward's dlogits launch covers one dW window, so the window's
+  // chunks must be bucketed at once: a window never exceeds the prep group.
+  // Every pass takes the same window, so the one-pass call contracts dW over
+  // the same rows in the same order as the backward.
   int64_t window = kDwRows / q.C;
   if (window > kDwMaxWindow) window = kDwMaxWindow;
   if (window > n_chunks) window = n_chunks;
+  if (window > group) window = group;
   if (window < 1) window = 1;
   q.dw_window = static_cast<int>(window);
+  // Launches do not cross prep groups: the forward's logit GEMM covers
+  // fwd_group chunks (fwd_group_rows rows at most), the backward's one
+  // window, and the prep group is a whole number of either.
+  int64_t fwd_group = 1;
+  if (pass == KD_PASS_FWD) {
+    fwd_group = fwd_group_rows / q.C;
+    if (fwd_group > group) fwd_group = group;
+    if (fwd_group < 1) fwd_group = 1;
+    group = group / fwd_group * fwd_group;
+  } else if (pass == KD_PASS_BWD) {
+    group = group / window * window;
+  }
+  q.fwd_group = fwd_group;
+  q.prep_chunks = group;
   // dH = dlogits · W of a window has a short output (window rows × d) and a
   // long contraction (V): split the contraction so that enough workgroups
   // exist to fill the chip.
@@ -72,20 +96,17 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
   if (splits < 1) splits = 1;
   q.dh_splits = static_cast<int>(splits);
   // Launch grids, in workgroups of 256 threads: the logit tiles of a chunk
-  // (nb), one workgroup per row (teacher finish), four rows per workgroup
-  // (prep, combine), the dH and dW tiles of a window, and the streaming
-  // passes over a chunk's stored logits (one-pass loss, teacher cache).
+  // (nb; a launch of several chunks stays inside a prep group, which holds
+  // at most kPrepBuckets tiles), one workgroup per row (teacher finish), four
+  // rows per workgroup (prep, combine), the dH and dW tiles of a window, and
+  // the streaming passes over a chunk's stored logits (one-pass loss,
+  // teacher cache).
   const int64_t dh_grid = (q.win_rows_pad / kTileM) * cdiv(d, kTileM) * q.dh_splits;
   const int64_t dw_grid = cdiv(d, kTileM) * q.nVt;
   const int64_t stream_grid = q.C * cdiv(q.V_pad, kStreamCols);
   if (q.nb > kMaxBlocks || q.C > kMaxBlocks || dh_grid > kMaxBlocks || dw_grid > kMaxBlocks ||
       ((pass == KD_PASS_FWD_BWD || pass == KD_PASS_TEACHER) && stream_grid > kMaxBlocks))
     return KD_ERR_UNSUPPORTED;
-  int64_t group = kPrepBuckets / q.nb;
-  if (group > kPrepRows / q.C) group = kPrepRows / q.C;
-  if (group > n_chunks) group = n_chunks;
-  if (group < 1) group = 1;
-  q.prep_chunks = group;
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -109,7 +130,10 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
     q.off_recs = take(8 * size_t(q.prep_chunks * q.C * K));
     q.off_rowS = take(sizeof(float) * size_t(q.prep_chunks * q.C));
   }
-  q.off_ht = dtype == KD_BF16 ? take(size_t(es) * size_t(d) * size_t(q.C_pad)) : 0;
+  // The transposed chunks of one logit launch: fwd_group chunks in the
+  // forward, one window in the backward, one chunk otherwise.
+  const int64_t ht_chunks = pass == KD_PASS_FWD ? q.fwd_group : pass == KD_PASS_BWD ? q.dw_window : 1;
+  q.off_ht = dtype == KD_BF16 ? take(size_t(es) * size_t(ht_chunks) * size_t(d) * size_t(q.C_pad)) : 0;
   q.off_z = 0;
   if (pass == KD_PASS_TEACHER) {
     // The chunk's logits (float32, [C][V_pad]), tile partials, lse, τ, and
@@ -122,8 +146,10 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
     q.off_cnt = take(sizeof(int32_t) * size_t(q.C_pad) * size_t(cdiv(q.V_pad, kStreamCols)));
     q.off_cand = take(8 * size_t(q.C_pad) * size_t(q.V_pad));
   } else if (pass == KD_PASS_FWD) {
-    q.off_zhit = take(sizeof(float) * size_t(q.C * K));
-    q.off_part = take(8 * size_t(q.C_pad * q.nVt));
+    // z at the cached ids and the tile partials of one launch, rows of its
+    // chunks back to back.
+    q.off_zhit = take(sizeof(float) * size_t(q.fwd_group * q.C * K));
+    q.off_part = take(8 * size_t((q.fwd_group - 1) * q.C + q.C_pad) * size_t(q.nVt));
     q.off_loss = take(sizeof(float) * size_t(N > 0 ? N : 1));
     q.off_dl = q.off_dhpart = 0;
   } else {

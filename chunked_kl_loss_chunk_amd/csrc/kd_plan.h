@@ -26,6 +26,10 @@ constexpr int kDhTargetTiles = 768;
 // pass: at most kPrepBuckets buckets and kPrepRows rows per group.
 constexpr int64_t kPrepBuckets = int64_t(1) << 20;
 constexpr int64_t kPrepRows = 65536;
+// The forward projects up to kFwdGroupRows rows (whole chunks, at least one)
+// in one launch of the logit GEMM, and the backward one dW window per
+// launch; neither launch crosses a prep group.
+constexpr int64_t kFwdGroupRows = 16384;
 // dW is contracted over a window of consecutive chunks at once: its fp32
 // read-modify-write of V×d happens once per window instead of once per chunk,
 // for a backward scratch of window × chunk × V dlogits. The window covers
@@ -52,7 +56,9 @@ struct Plan {
   int64_t nVt;    // vocabulary tiles
   int64_t nMt;    // row tiles per chunk
   int64_t nb;     // hit buckets per chunk = nMt * nVt
-  int64_t prep_chunks;  // chunks bucketed by one prep pass
+  int64_t prep_chunks;  // chunks bucketed by one prep pass (a multiple of fwd_group
+                        // for the forward, of dw_window for the backward)
+  int64_t fwd_group;    // forward: chunks per logit GEMM launch (1 for the other passes)
   int64_t kt_d;   // stages along d   (d * es / kStageRowBytes, rounded up)
   int64_t kt_v;   // stages along V_pad
   int dh_splits;  // split-K factor of the dH contraction (once per dW window)
@@ -61,7 +67,7 @@ struct Plan {
   // byte offsets inside the workspace (all 256-byte aligned)
   size_t off_counts, off_offsets, off_recs, off_rowS, off_zhit, off_part, off_loss, off_flag;
   size_t off_dl, off_dhpart;
-  size_t off_ht;      // bf16: the chunk of H transposed, [d][C_pad]
+  size_t off_ht;      // bf16: the chunks of one launch transposed, each [d][C_pad]
   size_t off_gscale;  // backward: the device scalar g (sum) or g / Σw (mean)
   // teacher cache producer: per-row lse, threshold, candidate count, candidates
   size_t off_lse, off_tau, off_cnt, off_cand;
@@ -71,9 +77,11 @@ struct Plan {
 };
 
 // Fills *p for the given pass (0 forward, 1 backward, 2 teacher cache,
-// 3 loss and gradients in one call).
+// 3 loss and gradients in one call). The forward's logit launches cover at
+// most fwd_group_rows rows (whole chunks, at least one chunk); a smaller cap
+// gives the same results in a smaller workspace.
 // Returns a kd_status.
 int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, int dtype,
-              Plan* p);
+              Plan* p, int64_t fwd_group_rows = kFwdGroupRows);
 
 }  // namespace kd

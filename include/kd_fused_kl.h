@@ -97,8 +97,13 @@ const char* kd_status_str(int status);
  * min(4, max(1, 4096 / chunk)) chunks; dW is contracted once per window. It
  * grows with the chunk, never with N × V. The forward and backward passes
  * also bucket the cached entries of up to 65,536 positions at a time (about
- * 8·K bytes per position). KD_PASS_FWD_BWD needs the backward's window and
- * one chunk of float32 logits (chunk × V × 4 bytes), and no buckets.
+ * 8·K bytes per position). One launch of the forward's logit GEMM covers up
+ * to 16,384 positions (whole chunks, at least one), and the forward holds
+ * their logsumexp partials (8 bytes per position and 256 vocabulary entries)
+ * and, in bf16, their transposed rows of H (2·d bytes per position); the
+ * backward holds the transposed rows of one window. KD_PASS_FWD_BWD needs
+ * the backward's window and one chunk of float32 logits (chunk × V × 4
+ * bytes), and no buckets.
  */
 size_t kd_fused_kl_workspace_bytes(int pass, int64_t N, int64_t d, int64_t V, int64_t K,
                                    int64_t chunk, int dtype);
@@ -115,7 +120,8 @@ size_t kd_fused_kl_workspace_bytes(int pass, int64_t N, int64_t d, int64_t V, in
  *  lse       [N] float32 — log Σ_j exp z_rj, saved for the backward pass.
  *  loss_sum  [1] float32 — Σ_r loss_tok[r], reduced in a fixed order.
  *
- * N = 0 writes loss_sum = 0. Rows are processed `chunk` at a time.
+ * N = 0 writes loss_sum = 0. Rows are processed `chunk` at a time; one
+ * launch of the logit GEMM projects the chunks of up to 16,384 rows.
  *
  * Returns KD_ERR_UNSUPPORTED for sizes the kernels do not take: K > 16383,
  * d > 2^20, N >= 2^31, a padded vocabulary row of 8 MiB or more
@@ -192,17 +198,20 @@ int kd_fused_kl_bwd_ex(const void* H, const void* W, int dtype, const int32_t* t
  *
  * Arguments, results and errors are those of kd_fused_kl_fwd_ex with the
  * workspace left out. The scratch the forward needs (the bucketed cache of a
- * group of chunks, the transposed chunk of H, the tile partials, and the
+ * group of chunks, the transposed chunks of H, the tile partials, and the
  * per-position losses when loss_tok is NULL) lives instead in a device array
  * held by the library: KD_NOALLOC_SCRATCH_BYTES bytes on every GPU the
- * library runs on, kept until the process ends. Sizes whose forward
- * workspace, kd_fused_kl_workspace_bytes(KD_PASS_FWD, ...), exceeds it are
- * rejected with KD_ERR_WORKSPACE before anything is enqueued. 64 MiB holds
- * the forward of the 8K-token head (17 MiB), of 32,768 tokens at d = 3072,
- * V = 128,256, K = 100, chunk 2048 (46 MiB) and of the 201,088-token head at
- * the same N (50 MiB); from 65,536 tokens at K = 100 the bucketed cache alone
- * takes 52 MiB and the call is rejected. The stream must belong to the
- * current device (KD_ERR_INVALID_ARG otherwise).
+ * library runs on, kept until the process ends. When the forward workspace,
+ * kd_fused_kl_workspace_bytes(KD_PASS_FWD, ...), exceeds it, the call
+ * projects one chunk per launch of the logit GEMM instead of a group of
+ * chunks: the same results bit for bit, from a smaller scratch. Sizes that
+ * exceed it even so are rejected with KD_ERR_WORKSPACE before anything is
+ * enqueued. 64 MiB holds the forward of the 8K-token head (17 MiB one chunk
+ * per launch), of 32,768 tokens at d = 3072, V = 128,256, K = 100, chunk
+ * 2048 (46 MiB) and of the 201,088-token head at the same N (50 MiB); from
+ * 65,536 tokens at K = 100 the bucketed cache alone takes 52 MiB and the call
+ * is rejected. The stream must belong to the current device
+ * (KD_ERR_INVALID_ARG otherwise).
  *
  * The first call on a device looks up that device's copy of the array
  * (hipGetSymbolAddress); make it once outside graph capture. No call
@@ -330,14 +339,14 @@ int kd_cast_f32_to_bf16(const float* src, void* dst, int64_t n, void* stream);
  * (total_ms[KD_KERNEL_CLASSES]) and launch counts
  * (launches[KD_KERNEL_CLASSES]), and clears the record. A "launch" of
  * KD_KERNEL_PREP is the three prep kernels of one group of chunks, or the
- * transpose of one chunk of H. The logit pass of the teacher cache and of
+ * transpose of the chunks of H one logit launch reads. The logit pass of the teacher cache and of
  * kd_fused_kl_fwd_bwd, which also store the logits, count as
  * KD_KERNEL_FWD_LOGITS; their streaming passes over the stored logits as
  * KD_KERNEL_DL_STREAM. Global state, not thread-safe; this is the one entry
  * point that synchronises (with its own events).
  */
 enum {
-  KD_KERNEL_PREP = 0,         /* bucket top-K entries; transpose a chunk of H */
+  KD_KERNEL_PREP = 0,         /* bucket top-K entries; transpose chunks of H  */
   KD_KERNEL_FWD_LOGITS = 1,   /* fused logit tile + logsumexp partials        */
   KD_KERNEL_BWD_DLOGITS = 2,  /* recomputed logit tile -> dlogits             */
   KD_KERNEL_BWD_DH = 3,       /* dH = dlogits W                               */

@@ -13,8 +13,11 @@
 //   flag            256 B
 //   counts          prep_chunks·nb int32        offsets  prep_chunks·nb + 1 int32
 //   recs            prep_chunks·C·K × 8 B       rowS     prep_chunks·C floats (one-pass: C)
-//   ht (bf16)       d × C_pad elements          zhit     C·K floats (forward)
-//   part            C_pad·nVt × 8 B             loss     max(N, 1) floats
+//   ht (bf16)       L·d·C_pad elements, L the chunks of one logit launch:
+//                   fwd_group (forward), dw_window (backward), else 1
+//   zhit            fwd_group·C·K floats (forward)
+//   part            ((fwd_group − 1)·C + C_pad)·nVt × 8 B (forward; else fwd_group = 1)
+//   loss            max(N, 1) floats
 //   z               C·V_pad floats              lse, tau C_pad floats each
 //   cnt             C_pad·⌈V_pad/8192⌉ int32    cand     C_pad·V_pad × 8 B
 //   gscale          256 B
@@ -50,10 +53,12 @@ void fail(const char* what, int pass, int64_t N, int64_t d, int64_t V, int64_t K
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Checks one call; returns its status.
-int check(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, int dt) {
+// Checks one call, with the forward's logit launches capped at `cap` rows;
+// returns its status.
+int check(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, int dt,
+          int64_t cap = kd::kFwdGroupRows) {
   kd::Plan p;
-  const int st = kd::make_plan(pass, N, d, V, K, chunk, dt, &p);
+  const int st = kd::make_plan(pass, N, d, V, K, chunk, dt, &p, cap);
   if (st != KD_OK) return st;
   const size_t es = dt == KD_BF16 ? 2 : 4;
   const int64_t C = std::min(chunk, std::max<int64_t>(N, 1));
@@ -74,6 +79,19 @@ int check(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, i
       (p.prep_chunks > 1 && (p.prep_chunks * p.nb > kd::kPrepBuckets ||
                              p.prep_chunks * C > kd::kPrepRows)))
     fail("prep group", pass, N, d, V, K, chunk, dt, std::to_string(p.prep_chunks));
+  // Launches never cross a prep group: the forward's logit launch covers
+  // fwd_group chunks, the backward's dlogits launch one window.
+  if (p.fwd_group < 1 || (pass != KD_PASS_FWD && p.fwd_group != 1) ||
+      (p.fwd_group > 1 && p.fwd_group * C > cap) ||
+      (pass == KD_PASS_FWD && p.prep_chunks % p.fwd_group != 0) ||
+      (pass == KD_PASS_BWD && p.prep_chunks % p.dw_window != 0))
+    fail("launch group", pass, N, d, V, K, chunk, dt,
+         std::to_string(p.fwd_group) + "/" + std::to_string(p.dw_window) + "/" +
+             std::to_string(p.prep_chunks));
+  const int64_t logit_chunks =
+      pass == KD_PASS_FWD ? p.fwd_group : pass == KD_PASS_BWD ? p.dw_window : 1;
+  if (logit_chunks * p.nb > kd::kMaxBlocks)
+    fail("logit grid", pass, N, d, V, K, chunk, dt, std::to_string(logit_chunks * p.nb));
 
   std::vector<Region> r;
   auto add = [&](const char* name, size_t off, size_t bytes) { r.push_back({name, off, bytes}); };
@@ -87,10 +105,11 @@ int check(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, i
     add("rowS", p.off_rowS, 4 * G * Cs);
   }
   if (pass == KD_PASS_FWD_BWD) add("rowS", p.off_rowS, 4 * Cs);
-  if (dt == KD_BF16) add("ht", p.off_ht, es * ds * Cp);
+  if (dt == KD_BF16) add("ht", p.off_ht, es * size_t(logit_chunks) * ds * Cp);
   if (pass == KD_PASS_FWD) {
-    add("zhit", p.off_zhit, 4 * Cs * Ks);
-    add("part", p.off_part, 8 * Cp * size_t(p.nVt));
+    const size_t Fg = size_t(p.fwd_group);
+    add("zhit", p.off_zhit, 4 * Fg * Cs * Ks);
+    add("part", p.off_part, 8 * ((Fg - 1) * Cs + Cp) * size_t(p.nVt));
     add("loss", p.off_loss, 4 * size_t(std::max<int64_t>(N, 1)));
   }
   if (pass == KD_PASS_TEACHER) {
@@ -148,6 +167,14 @@ int main() {
                 const int st = check(pass, N, d, V, K, c, dt);
                 if (st == KD_OK) {
                   ++ok;
+                  // One chunk per logit launch: the same call, valid too.
+                  if (pass == KD_PASS_FWD) {
+                    kd::Plan b;
+                    if (check(pass, N, d, V, K, c, dt, 0) != KD_OK ||
+                        kd::make_plan(pass, N, d, V, K, c, dt, &b, 0) != KD_OK ||
+                        b.fwd_group != 1)
+                      fail("one chunk per launch", pass, N, d, V, K, c, dt, "");
+                  }
                 } else {
                   ++rejected;
                   if (st != KD_ERR_INVALID_ARG && st != KD_ERR_UNSUPPORTED)

@@ -69,7 +69,10 @@ def test_workspace_size_rules(L):
     # the backward holds a window of chunks' dlogits: at least C x V_pad bf16
     V_pad = (128256 + 127) // 128 * 128
     assert wb >= 1024 * V_pad * 2
-    assert _ws(L, b, 8192, 3072, 128256, 100, 2048, bf) > wb
+    # the window covers 4096 rows with chunks of 1024 or 2048; one chunk of
+    # 8192 is a window of its own, twice as many rows
+    assert _ws(L, b, 8192, 3072, 128256, 100, 2048, bf) == wb
+    assert _ws(L, b, 8192, 3072, 128256, 100, 8192, bf) > wb
     # Past the prep group of 65,536 rows the backward workspace no longer
     # grows with N; below it, it grows by at most the bucketed cache entries
     # (8 bytes per entry, plus S_r) of the extra rows.
@@ -270,9 +273,12 @@ def test_one_pass_workspace(L):
     # the size does not grow with N
     w2 = ws(o, 262144, 3072, 128256, 100, 1024, bf)
     assert 0 <= w2 - w1 <= 4 * (262144 - 8192) + 256
-    # the extra over the backward is the chunk's logits (and small per-chunk buffers)
+    # the extra over the backward is the chunk's logits (and small per-chunk
+    # buffers), less the backward's bucketed entries and the three more
+    # transposed chunks of H its dlogits launch (one dW window) reads
     wb = ws(b, 8192, 3072, 128256, 100, 1024, bf)
-    assert 1024 * V_pad * 4 - (8 * 100 * 8192 + (1 << 22)) < w1 - wb <= 1024 * V_pad * 4 + (1 << 23)
+    held_by_bwd = 8 * 100 * 8192 + 3 * 3072 * 1024 * 2 + (1 << 22)
+    assert 1024 * V_pad * 4 - held_by_bwd < w1 - wb <= 1024 * V_pad * 4 + (1 << 23)
     # the streaming pass over the stored logits (one-pass loss and teacher
     # cache) takes a workgroup per 8192 logits of a row: chunk x V_pad / 8192
     # workgroups must stay below 2^24

@@ -30,12 +30,13 @@ def _counts(rec):
 
 
 # N = 1000 rows in chunks of 128: 7 full chunks and one of 104. V = 3000 gives
-# 12 vocabulary tiles, so one prep group covers all 8 chunks. The dW window is
-# min(4, 4096 / 128) = 4 chunks, so 2 windows; each window's dH is split over
-# the vocabulary (2 tiles of 256 window rows × 1 d tile, far below the 768
-# workgroups the split aims at) and reduced once.
+# 12 vocabulary tiles, so one prep group covers all 8 chunks, and so does one
+# launch of the forward's logit GEMM (up to 16,384 rows). The dW window is
+# min(4, 4096 / 128) = 4 chunks, so 2 windows, each with one dlogits launch;
+# each window's dH is split over the vocabulary (2 tiles of 256 window rows ×
+# 1 d tile, far below the 768 workgroups the split aims at) and reduced once.
 N, D, V, K, CHUNK = 1000, 64, 3000, 16, 128
-CHUNKS, WINDOWS = 8, 2
+CHUNKS, WINDOWS, FWD_LAUNCHES = 8, 2, 1
 
 
 def test_timing_follows_the_schedule_and_changes_nothing(kd):
@@ -68,12 +69,14 @@ def test_timing_follows_the_schedule_and_changes_nothing(kd):
     finally:
         L.kd_timing_enable(0)
 
-    # The forward: one prep pass and a transpose of H per chunk (bf16), a
-    # logit GEMM and a combine per chunk. The backward: the same prep, a
-    # recomputing dlogits GEMM per chunk, dW and dH (+ reduce) per window.
-    assert _counts(rec2) == {"prep": 2 * (1 + CHUNKS), "fwd_logits": CHUNKS,
-                             "bwd_dlogits": CHUNKS, "bwd_dh": WINDOWS, "bwd_dw": WINDOWS,
-                             "other": CHUNKS + WINDOWS, "dl_stream": 0}
+    # The forward: one prep pass; per launch of the logit GEMM (all 8 chunks)
+    # a transpose of its chunks of H (bf16), the GEMM and a combine. The
+    # backward: the same prep; per window a transpose, one recomputing
+    # dlogits GEMM over its chunks, dW and dH (+ reduce).
+    assert _counts(rec2) == {"prep": (1 + FWD_LAUNCHES) + (1 + WINDOWS),
+                             "fwd_logits": FWD_LAUNCHES, "bwd_dlogits": WINDOWS,
+                             "bwd_dh": WINDOWS, "bwd_dw": WINDOWS,
+                             "other": FWD_LAUNCHES + WINDOWS, "dl_stream": 0}
     # One pass: no prep groups, the storing logit GEMM, the combine and the
     # streaming dlogits pair per chunk, then the same windows.
     assert _counts(rec1) == {"prep": CHUNKS, "fwd_logits": CHUNKS, "bwd_dlogits": 0,
