@@ -540,12 +540,21 @@ def run_gemm_ceiling(steps, warmup, dev):
     L.kd_timing_enable(0)
     fused = {k: ks[k]["total_ms"] / ks[k]["launches"] for k in
              ("fwd_logits", "bwd_dlogits", "bwd_dh", "bwd_dw") if ks[k]["launches"]}
+    # A logit launch covers several chunks (the forward's group, the
+    # backward's window) and dH and dW one window each: compare per chunk
+    # and per window with the library's single GEMMs.
+    n_chunks = -(-cfg.N // C)
+    n_windows = -(-cfg.N // (win))
+    per_unit = {"fwd_logits per chunk": ks["fwd_logits"]["total_ms"] / (reps * n_chunks),
+                "bwd_dlogits per chunk": ks["bwd_dlogits"]["total_ms"] / (reps * n_chunks),
+                "bwd_dh per window": ks["bwd_dh"]["total_ms"] / (reps * n_windows),
+                "bwd_dw per window": ks["bwd_dw"]["total_ms"] / (reps * n_windows)}
     best_logits = min(lib_ms["logits (H_c . W^T)"]["ms"], lib_ms["logits (W . H_c^T)"]["ms"])
     ratio = {
-        "fwd_logits / best logits GEMM": fused["fwd_logits"] / best_logits,
-        "bwd_dlogits / best logits GEMM": fused["bwd_dlogits"] / best_logits,
-        "bwd_dh / dH GEMM": fused["bwd_dh"] / lib_ms["dH (dl . W)"]["ms"],
-        "bwd_dw / dW GEMM (fp32 out)": fused["bwd_dw"] / lib_ms["dW (dl^T . H_w, fp32 out)"]["ms"],
+        "fwd_logits / best logits GEMM": per_unit["fwd_logits per chunk"] / best_logits,
+        "bwd_dlogits / best logits GEMM": per_unit["bwd_dlogits per chunk"] / best_logits,
+        "bwd_dh / dH GEMM": per_unit["bwd_dh per window"] / lib_ms["dH (dl . W)"]["ms"],
+        "bwd_dw / dW GEMM (fp32 out)": per_unit["bwd_dw per window"] / lib_ms["dW (dl^T . H_w, fp32 out)"]["ms"],
     }
     print(json.dumps({
         "what": "hipBLASLt (torch.mm, bf16 operands) on the fused loss's contraction shapes, "
@@ -554,6 +563,7 @@ def run_gemm_ceiling(steps, warmup, dev):
                    "window": win},
         "torch_mm": lib_ms,
         "fused_avg_ms_per_launch": fused,
+        "fused_ms_per_chunk_or_window": per_unit,
         "fused_over_library": ratio,
         "reps": reps,
         "kernel_source_sha256": source_sha256(),
