@@ -210,67 +210,98 @@ __global__ __launch_bounds__(1024) void k_grad_scale(const float* __restrict__ g
 // prep: bucket the cached entries of a group of chunks by (chunk, row tile,
 // vocabulary tile)
 // --------------------------------------------------------------------------
-// Bucket of row `row` of the group (chunks of C rows, nMt row tiles each)
-// holding vocabulary id j.
-__device__ __forceinline__ int prep_bucket(int row, int j, int C, int nMt, int nVt) {
-  return ((row / C) * nMt + (row % C) / kTileM) * nVt + j / kTileN;
-}
+// One workgroup per 256-row token tile of the group: tile T = chunk·nMt + the
+// tile's index in its chunk, whose rows start at group row
+// row0 = chunk·C + 256·tile. The workgroup
+//   1. writes S_r = Σ_k p_rk over the valid entries of each of its rows, one
+//      wave per row, each lane summing k = lane, lane + 64, ... and then a
+//      butterfly over the wave (the order the one-pass combine repeats);
+//   2. counts its valid entries per vocabulary tile in LDS;
+//   3. scans the counts, and writes offsets[T·(nVt+1) + v] = the first
+//      record of vocabulary tile v (entry nVt ends the tile);
+//   4. scatters an 8-byte hit record per valid entry into its own range of
+//      recs, [row0·K, (row0 + rows)·K).
+// So no count, offset or record is shared between workgroups, and no global
+// atomics are needed. The order inside a bucket does not matter: every
+// record touches a distinct output element. Ids outside [0, V) raise `flag`
+// and are skipped; p = 0 entries are skipped.
+constexpr int kPrepThreads = 1024;
+constexpr int kPrepWaves = kPrepThreads / 64;
+constexpr int kPrepMaxVt = 16384;  // the plan keeps nVt below this (8 MiB rows)
+constexpr int kPrepUnroll = 4;     // entries (or rows) per thread (or wave) in flight
 
-// One wave per row. Counts valid entries per bucket and writes S_r = Σ_k p_rk.
-// Ids outside [0, V) raise `flag` and are skipped; p = 0 entries are skipped.
-__global__ __launch_bounds__(256) void k_prep_count(const int* __restrict__ idx,
-                                                    const float* __restrict__ logp, int64_t r0,
-                                                    int rows, int C, int nMt, int K, int V,
-                                                    int nVt, int* __restrict__ counts,
-                                                    float* __restrict__ rowS,
-                                                    int* __restrict__ flag) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const int* ir = idx + (r0 + row) * K;
-  const float* lr = logp + (r0 + row) * K;
-  float s = 0.f;
-  for (int k = lane; k < K; k += 64) {
-    const int j = ir[k];
-    const float p = __expf(lr[k]);
-    const bool ok = j >= 0 && j < V;
-    if (!ok) atomicOr(flag, 1);
-    if (ok && p > 0.f) {
-      s += p;
-      atomicAdd(&counts[prep_bucket(row, j, C, nMt, nVt)], 1);
+__global__ __launch_bounds__(kPrepThreads) void k_prep_tiles(const int* __restrict__ idx,
+                                                             const float* __restrict__ logp,
+                                                             int64_t r0, int rows, int C, int nMt,
+                                                             int K, int V, int nVt,
+                                                             int* __restrict__ offsets,
+                                                             uint2* __restrict__ recs,
+                                                             float* __restrict__ rowS,
+                                                             int* __restrict__ flag) {
+  __shared__ int cnt[kPrepMaxVt + 1];
+  __shared__ int wsum[kPrepWaves];
+  const int T = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c = T / nMt, row0 = c * C + (T % nMt) * kTileM;
+  const int chunk_end = rows < (c + 1) * C ? rows : (c + 1) * C;
+  const int left = chunk_end - row0;
+  const int nrows = left <= 0 ? 0 : left < kTileM ? left : kTileM;
+  const int* ir = idx + (r0 + row0) * K;
+  const float* lr = logp + (r0 + row0) * K;
+  for (int v = tid; v <= nVt; v += kPrepThreads) cnt[v] = 0;
+
+  // 1. S_r, kPrepUnroll rows per wave at a time.
+  for (int rb = w * kPrepUnroll; rb < nrows; rb += kPrepWaves * kPrepUnroll) {
+    float sr[kPrepUnroll];
+#pragma unroll
+    for (int u = 0; u < kPrepUnroll; ++u) sr[u] = 0.f;
+    for (int k = lane; k < K; k += 64) {
+#pragma unroll
+      for (int u = 0; u < kPrepUnroll; ++u) {
+        if (rb + u < nrows) {
+          const int j = ir[int64_t(rb + u) * K + k];
+          const float p = __expf(lr[int64_t(rb + u) * K + k]);
+          if (j >= 0 && j < V && p > 0.f) sr[u] += p;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPrepUnroll; ++u) {
+      const float t = wave_sum(sr[u]);
+      if (lane == 0 && rb + u < nrows) rowS[row0 + rb + u] = t;
     }
   }
-  s = wave_sum(s);
-  if (lane == 0) rowS[row] = s;
-}
+  __syncthreads();
 
-// Exclusive scan of the bucket counts (one workgroup). The counts pass
-// through LDS in tiles of 1024·kScanE: loaded and stored coalesced, each
-// thread scans kScanE consecutive counts, the threads' sums are scanned by
-// wave shuffles and the sixteen wave totals, and a running carry links the
-// tiles.
-constexpr int kScanE = 8;
-__global__ __launch_bounds__(1024) void k_prep_scan(const int* __restrict__ counts,
-                                                    int* __restrict__ offsets, int nb) {
-  constexpr int kTile = 1024 * kScanE;
-  __shared__ int tile[kTile];
-  __shared__ int wsum[16];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  int carry = 0;
-  for (int base = 0; base < nb; base += kTile) {
+  // 2. counts per vocabulary tile; the tile's entries are contiguous.
+  const int n = nrows * K;
+  for (int e0 = tid; e0 < n; e0 += kPrepUnroll * kPrepThreads) {
+    int j[kPrepUnroll];
+    float lp[kPrepUnroll];
 #pragma unroll
-    for (int e = 0; e < kScanE; ++e) {
-      const int i = base + e * 1024 + t;
-      tile[e * 1024 + t] = i < nb ? counts[i] : 0;
+    for (int u = 0; u < kPrepUnroll; ++u) {
+      const int e = e0 + u * kPrepThreads;
+      j[u] = e < n ? ir[e] : 0;
+      lp[u] = e < n ? lr[e] : kNegInf;
     }
-    __syncthreads();
-    int v[kScanE];
+#pragma unroll
+    for (int u = 0; u < kPrepUnroll; ++u) {
+      if (e0 + u * kPrepThreads >= n) continue;
+      const float p = __expf(lp[u]);
+      const bool ok = j[u] >= 0 && j[u] < V;
+      if (!ok) atomicOr(flag, 1);
+      if (ok && p > 0.f) atomicAdd(&cnt[j[u] / kTileN], 1);
+    }
+  }
+  __syncthreads();
+
+  // 3. exclusive scan of cnt[0, nVt): each thread a run of `per` counts,
+  // the runs' sums scanned by wave shuffles and the wave totals.
+  {
+    const int per = (nVt + kPrepThreads - 1) / kPrepThreads;
+    const int b = tid * per, e = b + per < nVt ? b + per : nVt;
     int sum = 0;
-#pragma unroll
-    for (int e = 0; e < kScanE; ++e) {
-      v[e] = tile[t * kScanE + e];
-      sum += v[e];
-    }
-    int incl = sum;  // inclusive scan of the threads' sums within the wave
+    for (int v = b; v < e; ++v) sum += cnt[v];
+    int incl = sum;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(incl, off);
@@ -278,50 +309,44 @@ __global__ __launch_bounds__(1024) void k_prep_scan(const int* __restrict__ coun
     }
     if (lane == 63) wsum[w] = incl;
     __syncthreads();
-    int before = 0, total = 0;
+    int run = incl - sum, total = 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      before += j < w ? wsum[j] : 0;
-      total += wsum[j];
+    for (int q = 0; q < kPrepWaves; ++q) {
+      run += q < w ? wsum[q] : 0;
+      total += wsum[q];
     }
-    int run = carry + before + incl - sum;
-#pragma unroll
-    for (int e = 0; e < kScanE; ++e) {
-      tile[t * kScanE + e] = run;
-      run += v[e];
+    for (int v = b; v < e; ++v) {
+      const int x = cnt[v];
+      cnt[v] = run;
+      run += x;
     }
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < kScanE; ++e) {
-      const int i = base + e * 1024 + t;
-      if (i < nb) offsets[i] = tile[e * 1024 + t];
-    }
-    carry += total;
-    __syncthreads();  // the tile and wsum are reused by the next round
+    if (tid == 0) cnt[nVt] = total;
   }
-  if (t == 0) offsets[nb] = carry;
-}
+  __syncthreads();
+  const int base = row0 * K;  // the tile's first record
+  int* const off = offsets + int64_t(T) * (nVt + 1);
+  for (int v = tid; v <= nVt; v += kPrepThreads) off[v] = base + cnt[v];
+  __syncthreads();
 
-// Scatter hit records into their buckets. Counting down leaves `counts` at
-// zero for the next chunk. The order inside a bucket does not matter: every
-// record touches a distinct output element.
-__global__ __launch_bounds__(256) void k_prep_scatter(const int* __restrict__ idx,
-                                                      const float* __restrict__ logp, int64_t r0,
-                                                      int rows, int C, int nMt, int K, int V,
-                                                      int nVt, int* __restrict__ counts,
-                                                      const int* __restrict__ offsets,
-                                                      uint2* __restrict__ recs) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const int* ir = idx + (r0 + row) * K;
-  const float* lr = logp + (r0 + row) * K;
-  for (int k = lane; k < K; k += 64) {
-    const int j = ir[k];
-    const float p = __expf(lr[k]);
-    if (j >= 0 && j < V && p > 0.f) {
-      const int b = prep_bucket(row, j, C, nMt, nVt);
-      const int pos = offsets[b] + atomicSub(&counts[b], 1) - 1;
-      recs[pos] = make_uint2(pack_hit((row % C) % kTileM, j % kTileN, k), __float_as_uint(p));
+  // 4. scatter, the scanned counts serving as cursors.
+  for (int e0 = tid; e0 < n; e0 += kPrepUnroll * kPrepThreads) {
+    int j[kPrepUnroll];
+    float lp[kPrepUnroll];
+#pragma unroll
+    for (int u = 0; u < kPrepUnroll; ++u) {
+      const int e = e0 + u * kPrepThreads;
+      j[u] = e < n ? ir[e] : 0;
+      lp[u] = e < n ? lr[e] : kNegInf;
+    }
+#pragma unroll
+    for (int u = 0; u < kPrepUnroll; ++u) {
+      const int e = e0 + u * kPrepThreads;
+      if (e >= n) continue;
+      const float p = __expf(lp[u]);
+      if (j[u] >= 0 && j[u] < V && p > 0.f) {
+        const int pos = base + atomicAdd(&cnt[j[u] / kTileN], 1);
+        recs[pos] = make_uint2(pack_hit(e / K, j[u] % kTileN, e % K), __float_as_uint(p));
+      }
     }
   }
 }
@@ -345,10 +370,10 @@ struct FwdArgs {
   ColOp Ht;  // the first chunk transposed, [d][C_pad] (bf16 path)
   int kt;   // stages along d
   int tiles_t, tiles_v;  // token tiles of all the launch's chunks; vocabulary tiles
-  int nch, C, nMt, nb;   // chunks, rows per chunk, token tiles and buckets per full chunk
+  int nch, C, nMt, nb;   // chunks, rows per chunk, token tiles and bucket offsets per full chunk
   int64_t ht_chunk;      // bytes from one chunk's transposed block to the next
   int rows, V, K, nVt;
-  const int* offsets;  // bucket offsets of the first chunk, nb per chunk
+  const int* offsets;  // bucket offsets of the first chunk: nVt + 1 per token tile, nb per chunk
   const uint2* recs;
   float* zhit;     // [rows, K]: z at the cached ids
   float2* part;    // [rows, nVt]: (max, Σexp) of each token over each vocabulary tile
@@ -576,7 +601,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd_logits(FwdArgs args) {
   if constexpr (STORE_Z)
     store_tile_logits(acc, region, a, t_base, v_base, wm, wn, lane);
   else
-    gather_hit_logits(acc, region, a, tt * a.nVt + vt, t_base, wm, wn, lane);
+    gather_hit_logits(acc, region, a, tt * (a.nVt + 1) + vt, t_base, wm, wn, lane);
 
   __syncthreads();
   if (t_base + tid < a.rows) {
@@ -737,10 +762,10 @@ struct DlArgs {
   ColOp Ht;  // bf16 path: the first chunk transposed, [d][C_pad]
   int kt;
   int tiles_t, tiles_v;  // token tiles of all the launch's chunks; vocabulary tiles
-  int nch, C, nMt, nb;   // chunks, rows per chunk, token tiles and buckets per full chunk
+  int nch, C, nMt, nb;   // chunks, rows per chunk, token tiles and bucket offsets per full chunk
   int64_t ht_chunk;      // bytes from one chunk's transposed block to the next
   int rows, V, nVt;
-  const int* offsets;  // bucket offsets of the first chunk, nb per chunk
+  const int* offsets;  // bucket offsets of the first chunk: nVt + 1 per token tile, nb per chunk
   const uint2* recs;
   const float* lse;   // the rows' lse (forward output)
   const float* rowS;  // the rows' S_r
@@ -791,7 +816,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs args) {
   const int wm = wave % kWM, wn = wave / kWM;
   const float g = *a.grad;
   const int vlim = a.V - (v_base + wm * kWTM);
-  const TileHits hits = hits_begin(a.offsets, a.recs, tt * a.nVt + vt, lane);
+  const TileHits hits = hits_begin(a.offsets, a.recs, tt * (a.nVt + 1) + vt, lane);
 
   // dl = g S_r exp(z − lse_r); tokens past the chunk give 0 (gs = 0), and so
   // do vocabulary rows past V (only in the last vocabulary tile).
@@ -1437,23 +1462,18 @@ void timed(int cls, hipStream_t st, F&& launch) {
   if (a && b) g_timing_recs.push_back(TimingRec{cls, a, b});
 }
 
-// Buckets the cached entries of the group of chunks starting at row r0.
+// Buckets the cached entries of the group of chunks starting at row r0: one
+// workgroup per 256-row token tile of the group.
 void launch_prep(const Plan& p, const Ws& ws, const int32_t* idx, const float* logp, int64_t r0,
                  hipStream_t st) {
   const int64_t left = p.N - r0, span = p.prep_chunks * p.C;
   const int rows = int(left < span ? left : span);
-  const int nblk = int(cdiv(rows, 4));
-  const int nbg = int(cdiv(rows, p.C) * p.nb);
+  const int ntiles = int(cdiv(rows, p.C) * p.nMt);
   timed(KD_KERNEL_PREP, st, [&] {
-    hipLaunchKernelGGL(k_prep_count, dim3(nblk), dim3(256), 0, st, idx, logp, r0, rows, int(p.C),
-                       int(p.nMt), int(p.K), int(p.V), int(p.nVt), ws.at<int>(p.off_counts),
-                       ws.at<float>(p.off_rowS), ws.at<int>(p.off_flag));
-    hipLaunchKernelGGL(k_prep_scan, dim3(1), dim3(1024), 0, st, ws.at<int>(p.off_counts),
-                       ws.at<int>(p.off_offsets), nbg);
-    hipLaunchKernelGGL(k_prep_scatter, dim3(nblk), dim3(256), 0, st, idx, logp, r0, rows,
+    hipLaunchKernelGGL(k_prep_tiles, dim3(ntiles), dim3(kPrepThreads), 0, st, idx, logp, r0, rows,
                        int(p.C), int(p.nMt), int(p.K), int(p.V), int(p.nVt),
-                       ws.at<int>(p.off_counts), ws.at<int>(p.off_offsets),
-                       ws.at<uint2>(p.off_recs));
+                       ws.at<int>(p.off_offsets), ws.at<uint2>(p.off_recs),
+                       ws.at<float>(p.off_rowS), ws.at<int>(p.off_flag));
   });
 }
 
@@ -1490,7 +1510,7 @@ void set_chunk_group(Args& a, const Plan& p, const void* H, const void* W, int64
   a.nch = nch;
   a.C = int(p.C);
   a.nMt = int(p.nMt);
-  a.nb = int(p.nb);
+  a.nb = int(p.nbo);
   a.ht_chunk = p.d * p.C_pad * 2;
   a.tiles_t = int((nch - 1) * p.nMt + cdiv(rows - int64_t(nch - 1) * p.C, kBN));
   a.tiles_v = int(p.nVt);
@@ -1500,8 +1520,6 @@ void set_chunk_group(Args& a, const Plan& p, const void* H, const void* W, int64
 }
 
 void launch_reset(const Plan& p, const Ws& ws, hipStream_t st) {
-  hipLaunchKernelGGL(k_fill_i32, dim3(cdiv(p.prep_chunks * p.nb, 256)), dim3(256), 0, st,
-                     ws.at<int>(p.off_counts), int64_t(p.prep_chunks * p.nb), 0);
   hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, st, ws.at<int>(p.off_flag), int64_t(64), 0);
 }
 
@@ -1528,7 +1546,7 @@ int run_fwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
                                                rows, st)
                            : ColOp{});
       a.K = int(p.K);
-      a.offsets = ws.at<int>(p.off_offsets) + slot * p.nb;
+      a.offsets = ws.at<int>(p.off_offsets) + slot * p.nbo;
       a.recs = ws.at<uint2>(p.off_recs);
       a.zhit = ws.at<float>(p.off_zhit);
       a.part = ws.at<float2>(p.off_part);
@@ -1634,7 +1652,7 @@ int run_bwd(const Plan& p, const void* H, const void* W, const int32_t* idx, con
                     BF16 ? chunks_transposed(p, ws, static_cast<const char*>(H) + r0 * row_bytes,
                                              rows, st)
                          : ColOp{});
-    a.offsets = ws.at<int>(p.off_offsets) + slot * p.nb;
+    a.offsets = ws.at<int>(p.off_offsets) + slot * p.nbo;
     a.recs = ws.at<uint2>(p.off_recs);
     a.lse = lse + r0;
     a.rowS = ws.at<float>(p.off_rowS) + slot * p.C;

@@ -11,7 +11,7 @@
 // Region sizes are the extents the kernels index, stated here from their
 // launch shapes:
 //   flag            256 B
-//   counts          prep_chunks·nb int32        offsets  prep_chunks·nb + 1 int32
+//   offsets         prep_chunks·nMt·(nVt + 1) int32
 //   recs            prep_chunks·C·K × 8 B       rowS     prep_chunks·C floats (one-pass: C)
 //   ht (bf16)       L·d·C_pad elements, L the chunks of one logit launch:
 //                   fwd_group (forward), dw_window (backward), else 1
@@ -65,7 +65,7 @@ int check(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, i
   // the derived sizes
   if (p.C != C || p.C_pad % 256 != 0 || p.C_pad < C || p.C_pad - C >= 256 || p.V_pad % 256 != 0 ||
       p.V_pad < V || p.V_pad - V >= 256 || p.nVt * 256 != p.V_pad || p.nMt * 256 != p.C_pad ||
-      p.nb != p.nMt * p.nVt)
+      p.nb != p.nMt * p.nVt || p.nbo != p.nMt * (p.nVt + 1) || p.nVt > 16383)
     fail("sizes", pass, N, d, V, K, chunk, dt, "");
   const int64_t n_chunks = N > 0 ? cdiv(N, C) : 1;
   if (p.dw_window < 1 || p.dw_window > kd::kDwMaxWindow || p.dw_window > n_chunks ||
@@ -99,8 +99,7 @@ int check(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, i
   const size_t Vp = size_t(p.V_pad), Ks = size_t(K), ds = size_t(d);
   add("flag", p.off_flag, 256);
   if (pass == KD_PASS_FWD || pass == KD_PASS_BWD) {
-    add("counts", p.off_counts, 4 * G * size_t(p.nb));
-    add("offsets", p.off_offsets, 4 * (G * size_t(p.nb) + 1));
+    add("offsets", p.off_offsets, 4 * G * size_t(p.nMt) * size_t(p.nVt + 1));
     add("recs", p.off_recs, 8 * G * Cs * Ks);
     add("rowS", p.off_rowS, 4 * G * Cs);
   }

@@ -140,6 +140,30 @@ def test_multiple_windows(kd, N, d, V, K, dtype, chunk):
     assert_parity(got, ref, dtype, f"{N},{d},{V},{K},{dtype},{chunk}")
 
 
+@pytest.mark.parametrize("N,d,V,K,dtype,chunk", [
+    # chunks of 4096: the forward projects 4 chunks per launch (16,384 rows),
+    # so 5 chunks take two launches, and the forward's prep groups follow
+    # them (4 chunks, then 1); the backward's windows are single chunks
+    (17000, 64, 1000, 8, "f32", 4096),
+    # chunks of 1000 (not a multiple of the 256-row tile): 17 chunks, a
+    # forward launch of 16 and one of 1, prep groups of 16 and 1 in both
+    # passes, and backward windows of 4 chunks up to the second prep group
+    (17000, 72, 1000, 8, "bf16", 1000),
+])
+def test_several_logit_launches_and_prep_groups(kd, N, d, V, K, dtype, chunk):
+    H, W, idx, logp = _case(N, d, V, K, dtype, seed=N + chunk)
+    got = run_hip(kd, H, W, idx, logp, chunk, grad=0.8)
+    ref = oracle.fused_kl_reference(H, W, idx, logp, grad=0.8)
+    assert_parity(got, ref, dtype, f"{N},{d},{V},{K},{dtype},{chunk}")
+    # the same results with one chunk per call's worth of rows: chunking
+    # changes the schedule, never the per-row values
+    Hd, Wd, id_, lp = _to_dev(H, W, idx, logp)
+    _, tok_a, lse_a = kd.kl_forward(Hd, Wd, id_, lp, chunk)
+    _, tok_b, lse_b = kd.kl_forward(Hd[: chunk], Wd, id_[: chunk], lp[: chunk], chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(tok_a[: chunk], tok_b) and torch.equal(lse_a[: chunk], lse_b)
+
+
 def test_neg_inf_logprob_contributes_nothing(kd):
     H, W, idx, logp = _case(96, 64, 700, 6, "f32", seed=5)
     logp = logp.clone()
