@@ -10,10 +10,13 @@
 //
 // Per chunk of C positions ([P1] "As duas mudanças"; [P4] 为什么蒸馏恢复代价高昂,
 // "Fused chunked KL" paragraph: project one chunk, fold it into the running
-// loss, discard it; recompute it in backward):
+// loss, discard it; recompute it in backward). One launch of a logit kernel
+// covers a group of consecutive chunks (the forward's up to 16,384 rows, the
+// backward's dW window) and walks them chunk by chunk:
 //
 //  forward   prep    bucket the top-K entries of a group of chunks by logit
-//                    tile (one pass per group of up to 65,536 rows); S_r
+//                    tile (one kernel per group of up to 65,536 rows, a
+//                    workgroup per 256-row token tile); S_r
 //            logits  z tile = H_c Wᵀ on MFMA; per tile: row max and Σexp
 //                    (online logsumexp partials) and z at the cached ids
 //            combine lse_r from the partials; L_r = Σp·logp − Σp·z + S_r·lse_r;
