@@ -174,6 +174,21 @@ def test_binding_fails_loudly_without_gpu_tensors():
                        torch.zeros(4, 2), chunk=2)
 
 
+def test_noalloc_falls_back_to_one_chunk_per_launch_at_the_8k_head(L):
+    """At the 8K head the forward projects all 8 chunks in one launch, whose
+    workspace exceeds the no-allocation scratch; one chunk per launch fits. So
+    the GPU test of the no-allocation forward at that head runs the
+    fallback (tests/test_zz_no_alloc.py)."""
+    grouped = L.kd_fused_kl_workspace_bytes(_lib.KD_PASS_FWD, 8192, 3072, 128256, 100, 1024,
+                                            _lib.KD_BF16)
+    assert grouped > _lib.KD_NOALLOC_SCRATCH_BYTES
+    # one chunk per launch: the bucketed cache of the group, one transposed
+    # chunk, and one chunk's z at the cached ids and partials
+    one_chunk = (8192 * 100 * 8 + 8 * 4 * 502 * 4 + 8192 * 4 + 3072 * 1024 * 2
+                 + 1024 * 100 * 4 + 1024 * 501 * 8)
+    assert one_chunk < _lib.KD_NOALLOC_SCRATCH_BYTES
+
+
 def test_vocabulary_row_limit(L):
     """The GEMM loaders take 32-bit offsets within a 256-row tile: a padded
     vocabulary row must stay under 8 MiB in the compute dtype."""

@@ -164,6 +164,22 @@ def test_several_logit_launches_and_prep_groups(kd, N, d, V, K, dtype, chunk):
     assert torch.equal(tok_a[: chunk], tok_b) and torch.equal(lse_a[: chunk], lse_b)
 
 
+@pytest.mark.parametrize("dtype,V,d", [
+    ("bf16", 4194048, 16),  # the largest vocabulary in bf16: 16,383 vocabulary tiles
+    ("f32", 2096896, 8),    # and in float32: 8,191 tiles (a padded row just under 8 MiB)
+])
+def test_largest_vocabulary(kd, dtype, V, d):
+    # The prep kernel counts a token tile's entries per vocabulary tile in LDS
+    # (up to 16,383 counters) and the loaders address a 256-row tile of the
+    # dlogits with 32-bit offsets: both at their limits here. Three chunks
+    # (16, 16 and 8 rows) in one forward launch and one dW window.
+    N, K, chunk = 40, 8, 16
+    H, W, idx, logp = _case(N, d, V, K, dtype, seed=V % 1000 + d)
+    got = run_hip(kd, H, W, idx, logp, chunk, grad=1.1)
+    ref = oracle.fused_kl_reference(H, W, idx, logp, grad=1.1)
+    assert_parity(got, ref, dtype, f"V={V},{dtype}")
+
+
 def test_neg_inf_logprob_contributes_nothing(kd):
     H, W, idx, logp = _case(96, 64, 700, 6, "f32", seed=5)
     logp = logp.clone()
