@@ -213,126 +213,61 @@ __global__ __launch_bounds__(1024) void k_grad_scale(const float* __restrict__ g
 // prep: bucket the cached entries of a group of chunks by (chunk, row tile,
 // vocabulary tile)
 // --------------------------------------------------------------------------
-// One workgroup per 256-row token tile of the group: tile T = chunk·nMt + the
-// tile's index in its chunk, whose rows start at group row
-// row0 = chunk·C + 256·tile. The workgroup
-//   1. writes S_r = Σ_k p_rk over the valid entries of each of its rows, one
-//      wave per row, each lane summing k = lane, lane + 64, ... and then a
-//      butterfly over the wave (the order the one-pass combine repeats);
-//   2. counts its valid entries per vocabulary tile in LDS;
-//   3. scans the counts, and writes offsets[T·(nVt+1) + v] = the first
-//      record of vocabulary tile v (entry nVt ends the tile);
-//   4. scatters an 8-byte hit record per valid entry into its own range of
-//      recs, [row0·K, (row0 + rows)·K).
-// So no count, offset or record is shared between workgroups, and no global
-// atomics are needed. The order inside a bucket does not matter: every
-// record touches a distinct output element. Ids outside [0, V) raise `flag`
-// and are skipped; p = 0 entries are skipped.
+// Token tile T = chunk·nMt + the tile's index in its chunk; its rows start at
+// group row row0 = chunk·C + 256·tile, and its records fill their own range
+// of recs, [row0·K, (row0 + rows)·K). offsets[T·(nVt+1) + v] is the first
+// record of vocabulary tile v, offsets[T·(nVt+1) + nVt] the end of the
+// tile's records. The order inside a bucket does not matter: every record
+// touches a distinct output element.
+//
+// Two launches over (token tile, vocabulary slice) workgroups, so that a
+// group of few token tiles still fills the chip: slice s of a tile covers
+// its vocabulary tiles [s·span, (s+1)·span). Each workgroup reads all of its
+// tile's entries and keeps those of its slice.
+//   k_prep_count   counts the slice's valid entries per vocabulary tile in
+//                  LDS into counts[T·nVt + v]; it also writes S_r for the
+//                  tile rows r ≡ s (mod slices), one wave per row, each lane
+//                  summing k = lane, lane + 64, ... and then a butterfly over
+//                  the wave (the order the one-pass combine repeats).
+//   k_prep_scatter sums the counts of the tile's earlier slices, scans its
+//                  own in LDS, writes the offsets, and scatters the slice's
+//                  8-byte hit records.
+// Ids outside [0, V) raise `flag` (slice 0 reports them) and are skipped;
+// p = 0 entries are skipped.
 constexpr int kPrepThreads = 1024;
 constexpr int kPrepWaves = kPrepThreads / 64;
 constexpr int kPrepMaxVt = 16384;  // the plan keeps nVt below this (8 MiB rows)
 constexpr int kPrepUnroll = 4;     // entries (or rows) per thread (or wave) in flight
+constexpr int kPrepTargetBlocks = 256;  // workgroups a prep launch aims at
 
-__global__ __launch_bounds__(kPrepThreads) void k_prep_tiles(const int* __restrict__ idx,
-                                                             const float* __restrict__ logp,
-                                                             int64_t r0, int rows, int C, int nMt,
-                                                             int K, int V, int nVt,
-                                                             int* __restrict__ offsets,
-                                                             uint2* __restrict__ recs,
-                                                             float* __restrict__ rowS,
-                                                             int* __restrict__ flag) {
-  __shared__ int cnt[kPrepMaxVt + 1];
-  __shared__ int wsum[kPrepWaves];
-  const int T = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int c = T / nMt, row0 = c * C + (T % nMt) * kTileM;
+struct PrepTile {
+  int T, s;        // token tile, vocabulary slice
+  int row0, rows;  // first group row, rows
+  int v0, v1;      // the slice's vocabulary tiles
+};
+
+__device__ __forceinline__ PrepTile prep_tile(int rows, int C, int nMt, int nVt, int span,
+                                              int slices) {
+  PrepTile t;
+  t.T = blockIdx.x / slices;
+  t.s = blockIdx.x % slices;
+  const int c = t.T / nMt;
+  t.row0 = c * C + (t.T % nMt) * kTileM;
   const int chunk_end = rows < (c + 1) * C ? rows : (c + 1) * C;
-  const int left = chunk_end - row0;
-  const int nrows = left <= 0 ? 0 : left < kTileM ? left : kTileM;
-  const int* ir = idx + (r0 + row0) * K;
-  const float* lr = logp + (r0 + row0) * K;
-  for (int v = tid; v <= nVt; v += kPrepThreads) cnt[v] = 0;
+  const int left = chunk_end - t.row0;
+  t.rows = left <= 0 ? 0 : left < kTileM ? left : kTileM;
+  t.v0 = t.s * span;
+  t.v1 = t.v0 + span < nVt ? t.v0 + span : nVt;
+  return t;
+}
 
-  // 1. S_r, kPrepUnroll rows per wave at a time.
-  for (int rb = w * kPrepUnroll; rb < nrows; rb += kPrepWaves * kPrepUnroll) {
-    float sr[kPrepUnroll];
-#pragma unroll
-    for (int u = 0; u < kPrepUnroll; ++u) sr[u] = 0.f;
-    for (int k = lane; k < K; k += 64) {
-#pragma unroll
-      for (int u = 0; u < kPrepUnroll; ++u) {
-        if (rb + u < nrows) {
-          const int j = ir[int64_t(rb + u) * K + k];
-          const float p = __expf(lr[int64_t(rb + u) * K + k]);
-          if (j >= 0 && j < V && p > 0.f) sr[u] += p;
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kPrepUnroll; ++u) {
-      const float t = wave_sum(sr[u]);
-      if (lane == 0 && rb + u < nrows) rowS[row0 + rb + u] = t;
-    }
-  }
-  __syncthreads();
-
-  // 2. counts per vocabulary tile; the tile's entries are contiguous.
-  const int n = nrows * K;
-  for (int e0 = tid; e0 < n; e0 += kPrepUnroll * kPrepThreads) {
-    int j[kPrepUnroll];
-    float lp[kPrepUnroll];
-#pragma unroll
-    for (int u = 0; u < kPrepUnroll; ++u) {
-      const int e = e0 + u * kPrepThreads;
-      j[u] = e < n ? ir[e] : 0;
-      lp[u] = e < n ? lr[e] : kNegInf;
-    }
-#pragma unroll
-    for (int u = 0; u < kPrepUnroll; ++u) {
-      if (e0 + u * kPrepThreads >= n) continue;
-      const float p = __expf(lp[u]);
-      const bool ok = j[u] >= 0 && j[u] < V;
-      if (!ok) atomicOr(flag, 1);
-      if (ok && p > 0.f) atomicAdd(&cnt[j[u] / kTileN], 1);
-    }
-  }
-  __syncthreads();
-
-  // 3. exclusive scan of cnt[0, nVt): each thread a run of `per` counts,
-  // the runs' sums scanned by wave shuffles and the wave totals.
-  {
-    const int per = (nVt + kPrepThreads - 1) / kPrepThreads;
-    const int b = tid * per, e = b + per < nVt ? b + per : nVt;
-    int sum = 0;
-    for (int v = b; v < e; ++v) sum += cnt[v];
-    int incl = sum;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
-    if (lane == 63) wsum[w] = incl;
-    __syncthreads();
-    int run = incl - sum, total = 0;
-#pragma unroll
-    for (int q = 0; q < kPrepWaves; ++q) {
-      run += q < w ? wsum[q] : 0;
-      total += wsum[q];
-    }
-    for (int v = b; v < e; ++v) {
-      const int x = cnt[v];
-      cnt[v] = run;
-      run += x;
-    }
-    if (tid == 0) cnt[nVt] = total;
-  }
-  __syncthreads();
-  const int base = row0 * K;  // the tile's first record
-  int* const off = offsets + int64_t(T) * (nVt + 1);
-  for (int v = tid; v <= nVt; v += kPrepThreads) off[v] = base + cnt[v];
-  __syncthreads();
-
-  // 4. scatter, the scanned counts serving as cursors.
-  for (int e0 = tid; e0 < n; e0 += kPrepUnroll * kPrepThreads) {
+// Visits the valid entries of the tile whose vocabulary tile is in the
+// slice: f(entry index within the tile, id, p). The tile's entries are
+// contiguous, kPrepUnroll per thread in flight.
+template <class F>
+__device__ __forceinline__ void prep_visit(const int* ir, const float* lr, int n, int V, int v0,
+                                           int v1, int* flag, F&& f) {
+  for (int e0 = threadIdx.x; e0 < n; e0 += kPrepUnroll * kPrepThreads) {
     int j[kPrepUnroll];
     float lp[kPrepUnroll];
 #pragma unroll
@@ -345,13 +280,135 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_tiles(const int* __restri
     for (int u = 0; u < kPrepUnroll; ++u) {
       const int e = e0 + u * kPrepThreads;
       if (e >= n) continue;
-      const float p = __expf(lp[u]);
-      if (j[u] >= 0 && j[u] < V && p > 0.f) {
-        const int pos = base + atomicAdd(&cnt[j[u] / kTileN], 1);
-        recs[pos] = make_uint2(pack_hit(e / K, j[u] % kTileN, e % K), __float_as_uint(p));
+      const bool ok = j[u] >= 0 && j[u] < V;
+      if (!ok) {
+        if (flag) atomicOr(flag, 1);
+        continue;
       }
+      const int vt = j[u] / kTileN;
+      if (vt < v0 || vt >= v1) continue;
+      const float p = __expf(lp[u]);
+      if (p > 0.f) f(e, j[u], p);
     }
   }
+}
+
+__global__ __launch_bounds__(kPrepThreads) void k_prep_count(const int* __restrict__ idx,
+                                                             const float* __restrict__ logp,
+                                                             int64_t r0, int rows, int C, int nMt,
+                                                             int K, int V, int nVt, int span,
+                                                             int slices, int* __restrict__ counts,
+                                                             float* __restrict__ rowS,
+                                                             int* __restrict__ flag) {
+  __shared__ int cnt[kPrepMaxVt];
+  const PrepTile t = prep_tile(rows, C, nMt, nVt, span, slices);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int* ir = idx + (r0 + t.row0) * K;
+  const float* lr = logp + (r0 + t.row0) * K;
+  for (int v = tid; v < t.v1 - t.v0; v += kPrepThreads) cnt[v] = 0;
+
+  // S_r of the tile rows s, s + slices, ...: kPrepUnroll rows per wave at a
+  // time, rows in the order of the tile.
+  const int nmine = t.rows > t.s ? (t.rows - t.s + slices - 1) / slices : 0;
+  for (int ib = w * kPrepUnroll; ib < nmine; ib += kPrepWaves * kPrepUnroll) {
+    float sr[kPrepUnroll];
+#pragma unroll
+    for (int u = 0; u < kPrepUnroll; ++u) sr[u] = 0.f;
+    for (int k = lane; k < K; k += 64) {
+#pragma unroll
+      for (int u = 0; u < kPrepUnroll; ++u) {
+        if (ib + u < nmine) {
+          const int64_t rr = t.s + int64_t(ib + u) * slices;
+          const int j = ir[rr * K + k];
+          const float p = __expf(lr[rr * K + k]);
+          if (j >= 0 && j < V && p > 0.f) sr[u] += p;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPrepUnroll; ++u) {
+      const float x = wave_sum(sr[u]);
+      if (lane == 0 && ib + u < nmine) rowS[t.row0 + t.s + (ib + u) * slices] = x;
+    }
+  }
+  __syncthreads();
+
+  prep_visit(ir, lr, t.rows * K, V, t.v0, t.v1, t.s == 0 ? flag : nullptr,
+             [&](int, int j, float) { atomicAdd(&cnt[j / kTileN - t.v0], 1); });
+  __syncthreads();
+  int* const out = counts + int64_t(t.T) * nVt + t.v0;
+  for (int v = tid; v < t.v1 - t.v0; v += kPrepThreads) out[v] = cnt[v];
+}
+
+__global__ __launch_bounds__(kPrepThreads) void k_prep_scatter(const int* __restrict__ idx,
+                                                               const float* __restrict__ logp,
+                                                               int64_t r0, int rows, int C,
+                                                               int nMt, int K, int V, int nVt,
+                                                               int span, int slices,
+                                                               const int* __restrict__ counts,
+                                                               int* __restrict__ offsets,
+                                                               uint2* __restrict__ recs) {
+  __shared__ int cnt[kPrepMaxVt + 1];
+  __shared__ int wsum[kPrepWaves];
+  const PrepTile t = prep_tile(rows, C, nMt, nVt, span, slices);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int* tc = counts + int64_t(t.T) * nVt;
+  const int nv = t.v1 - t.v0;
+
+  // The records of the tile's earlier slices come first.
+  int before = 0;
+  for (int v = tid; v < t.v0; v += kPrepThreads) before += tc[v];
+  // exclusive scan of the slice's counts: each thread a run of `per` counts,
+  // the runs' sums scanned by wave shuffles and the wave totals
+  const int per = (nv + kPrepThreads - 1) / kPrepThreads;
+  const int b = tid * per, e = b + per < nv ? b + per : nv;
+  int sum = 0;
+  for (int v = b; v < e; ++v) {
+    cnt[v] = tc[t.v0 + v];
+    sum += cnt[v];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  // one pass of wave totals for the earlier slices' sum, one for the scan
+  const int wb = __shfl_xor(before, 32) + before;
+  int btot = wb;
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) btot += __shfl_xor(btot, off);
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int run = incl - sum, total = 0;
+#pragma unroll
+  for (int q = 0; q < kPrepWaves; ++q) {
+    run += q < w ? wsum[q] : 0;
+    total += wsum[q];
+  }
+  __syncthreads();  // wsum is reused for the earlier slices' sum
+  if (lane == 0) wsum[w] = btot;
+  __syncthreads();
+  int base = t.row0 * K;
+#pragma unroll
+  for (int q = 0; q < kPrepWaves; ++q) base += wsum[q];
+  for (int v = b; v < e; ++v) {
+    const int x = cnt[v];
+    cnt[v] = run;
+    run += x;
+  }
+  __syncthreads();
+  int* const off = offsets + int64_t(t.T) * (nVt + 1);
+  for (int v = tid; v < nv; v += kPrepThreads) off[t.v0 + v] = base + cnt[v];
+  if (t.v1 == nVt && tid == 0) off[nVt] = base + total;
+
+  // scatter, the scanned counts serving as cursors
+  const int* ir = idx + (r0 + t.row0) * K;
+  const float* lr = logp + (r0 + t.row0) * K;
+  prep_visit(ir, lr, t.rows * K, V, t.v0, t.v1, nullptr, [&](int en, int j, float p) {
+    const int pos = base + atomicAdd(&cnt[j / kTileN - t.v0], 1);
+    recs[pos] = make_uint2(pack_hit(en / K, j % kTileN, en % K), __float_as_uint(p));
+  });
 }
 
 // --------------------------------------------------------------------------
@@ -1465,18 +1522,27 @@ void timed(int cls, hipStream_t st, F&& launch) {
   if (a && b) g_timing_recs.push_back(TimingRec{cls, a, b});
 }
 
-// Buckets the cached entries of the group of chunks starting at row r0: one
-// workgroup per 256-row token tile of the group.
+// Buckets the cached entries of the group of chunks starting at row r0: two
+// launches over (token tile, vocabulary slice) workgroups, with enough slices
+// per tile that a group of few token tiles still spreads over the chip.
 void launch_prep(const Plan& p, const Ws& ws, const int32_t* idx, const float* logp, int64_t r0,
                  hipStream_t st) {
-  const int64_t left = p.N - r0, span = p.prep_chunks * p.C;
-  const int rows = int(left < span ? left : span);
-  const int ntiles = int(cdiv(rows, p.C) * p.nMt);
+  const int64_t left = p.N - r0, span_rows = p.prep_chunks * p.C;
+  const int rows = int(left < span_rows ? left : span_rows);
+  const int64_t ntiles = cdiv(rows, p.C) * p.nMt;
+  int64_t slices = cdiv(kPrepTargetBlocks, ntiles);
+  if (slices > p.nVt) slices = p.nVt;
+  const int span = int(cdiv(p.nVt, slices));
+  slices = cdiv(p.nVt, span);  // no empty slice
+  const unsigned grid = unsigned(ntiles * slices);
   timed(KD_KERNEL_PREP, st, [&] {
-    hipLaunchKernelGGL(k_prep_tiles, dim3(ntiles), dim3(kPrepThreads), 0, st, idx, logp, r0, rows,
-                       int(p.C), int(p.nMt), int(p.K), int(p.V), int(p.nVt),
-                       ws.at<int>(p.off_offsets), ws.at<uint2>(p.off_recs),
-                       ws.at<float>(p.off_rowS), ws.at<int>(p.off_flag));
+    hipLaunchKernelGGL(k_prep_count, dim3(grid), dim3(kPrepThreads), 0, st, idx, logp, r0, rows,
+                       int(p.C), int(p.nMt), int(p.K), int(p.V), int(p.nVt), span, int(slices),
+                       ws.at<int>(p.off_counts), ws.at<float>(p.off_rowS), ws.at<int>(p.off_flag));
+    hipLaunchKernelGGL(k_prep_scatter, dim3(grid), dim3(kPrepThreads), 0, st, idx, logp, r0, rows,
+                       int(p.C), int(p.nMt), int(p.K), int(p.V), int(p.nVt), span, int(slices),
+                       ws.at<int>(p.off_counts), ws.at<int>(p.off_offsets),
+                       ws.at<uint2>(p.off_recs));
   });
 }
 

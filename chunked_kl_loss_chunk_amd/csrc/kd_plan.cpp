@@ -121,11 +121,12 @@ int make_plan(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chun
     // read per row (one-pass loss: S_r of one chunk), or there are none
     // (teacher cache).
     q.prep_chunks = 1;
-    q.off_offsets = q.off_recs = 0;
+    q.off_counts = q.off_offsets = q.off_recs = 0;
     q.off_rowS = pass == KD_PASS_FWD_BWD ? take(sizeof(float) * size_t(q.C)) : 0;
   } else {
-    // Prep buffers of one group of chunks: bucket offsets (chunk slot major,
-    // then token tile, nVt + 1 each), hit records, S_r.
+    // Prep buffers of one group of chunks: bucket counts (chunk slot major,
+    // then token tile, nVt each) and offsets (nVt + 1 each), hit records, S_r.
+    q.off_counts = take(sizeof(int32_t) * size_t(q.prep_chunks * q.nb));
     q.off_offsets = take(sizeof(int32_t) * size_t(q.prep_chunks * q.nbo));
     q.off_recs = take(8 * size_t(q.prep_chunks * q.C * K));
     q.off_rowS = take(sizeof(float) * size_t(q.prep_chunks * q.C));

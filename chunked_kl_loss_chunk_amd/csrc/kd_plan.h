@@ -67,7 +67,7 @@ struct Plan {
   int64_t win_rows_pad;  // rows of a full dW window, rounded up to kTileM
   int dw_window;  // chunks whose dlogits are held before one dW contraction
   // byte offsets inside the workspace (all 256-byte aligned)
-  size_t off_offsets, off_recs, off_rowS, off_zhit, off_part, off_loss, off_flag;
+  size_t off_counts, off_offsets, off_recs, off_rowS, off_zhit, off_part, off_loss, off_flag;
   size_t off_dl, off_dhpart;
   size_t off_ht;      // bf16: the chunks of one launch transposed, each [d][C_pad]
   size_t off_gscale;  // backward: the device scalar g (sum) or g / Σw (mean)

@@ -11,7 +11,7 @@
 // Region sizes are the extents the kernels index, stated here from their
 // launch shapes:
 //   flag            256 B
-//   offsets         prep_chunks·nMt·(nVt + 1) int32
+//   counts          prep_chunks·nb int32        offsets  prep_chunks·nMt·(nVt + 1) int32
 //   recs            prep_chunks·C·K × 8 B       rowS     prep_chunks·C floats (one-pass: C)
 //   ht (bf16)       L·d·C_pad elements, L the chunks of one logit launch:
 //                   fwd_group (forward), dw_window (backward), else 1
@@ -99,6 +99,7 @@ int check(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, i
   const size_t Vp = size_t(p.V_pad), Ks = size_t(K), ds = size_t(d);
   add("flag", p.off_flag, 256);
   if (pass == KD_PASS_FWD || pass == KD_PASS_BWD) {
+    add("counts", p.off_counts, 4 * G * size_t(p.nb));
     add("offsets", p.off_offsets, 4 * G * size_t(p.nMt) * size_t(p.nVt + 1));
     add("recs", p.off_recs, 8 * G * Cs * Ks);
     add("rowS", p.off_rowS, 4 * G * Cs);
