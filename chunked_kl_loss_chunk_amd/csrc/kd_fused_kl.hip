@@ -15,8 +15,8 @@
 // backward's dW window) and walks them chunk by chunk:
 //
 //  forward   prep    bucket the top-K entries of a group of chunks by logit
-//                    tile (one kernel per group of up to 65,536 rows, a
-//                    workgroup per 256-row token tile); S_r
+//                    tile (a count and a scatter launch per group of up to
+//                    65,536 rows, over token tile × vocabulary slice); S_r
 //            logits  z tile = H_c Wᵀ on MFMA; per tile: row max and Σexp
 //                    (online logsumexp partials) and z at the cached ids
 //            combine lse_r from the partials; L_r = Σp·logp − Σp·z + S_r·lse_r;

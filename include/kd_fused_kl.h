@@ -338,7 +338,7 @@ int kd_cast_f32_to_bf16(const float* src, void* dst, int64_t n, void* stream);
  * events, writes per kernel class the summed milliseconds
  * (total_ms[KD_KERNEL_CLASSES]) and launch counts
  * (launches[KD_KERNEL_CLASSES]), and clears the record. A "launch" of
- * KD_KERNEL_PREP is the prep kernel of one group of chunks, or the
+ * KD_KERNEL_PREP is the two prep kernels of one group of chunks, or the
  * transpose of the chunks of H one logit launch reads. The logit pass of the teacher cache and of
  * kd_fused_kl_fwd_bwd, which also store the logits, count as
  * KD_KERNEL_FWD_LOGITS; their streaming passes over the stored logits as
