@@ -169,10 +169,10 @@ def test_several_logit_launches_and_prep_groups(kd, N, d, V, K, dtype, chunk):
     ("f32", 2096896, 8),    # and in float32: 8,191 tiles (a padded row just under 8 MiB)
 ])
 def test_largest_vocabulary(kd, dtype, V, d):
-    # The prep kernel counts a token tile's entries per vocabulary tile in LDS
-    # (up to 16,383 counters) and the loaders address a 256-row tile of the
-    # dlogits with 32-bit offsets: both at their limits here. Three chunks
-    # (16, 16 and 8 rows) in one forward launch and one dW window.
+    # The loaders address a 256-row tile of the dlogits with 32-bit offsets,
+    # at their limit here, and the prep splits each token tile's 16,383 (or
+    # 8,191) vocabulary tiles over its slices. Three chunks (16, 16 and 8
+    # rows) in one forward launch and one dW window.
     N, K, chunk = 40, 8, 16
     H, W, idx, logp = _case(N, d, V, K, dtype, seed=V % 1000 + d)
     got = run_hip(kd, H, W, idx, logp, chunk, grad=1.1)
