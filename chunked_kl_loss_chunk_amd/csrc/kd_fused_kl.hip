@@ -67,6 +67,13 @@ struct Elt<false> {
   typedef float T;
 };
 
+// Two floats to two bf16 (round to nearest even) in one word, lo in the low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
 // Hit record of one cached teacher entry inside a logit tile.
 __device__ __forceinline__ uint32_t pack_hit(int row_in_tile, int col_in_tile, int k) {
   return uint32_t(row_in_tile) | (uint32_t(col_in_tile) << 8) | (uint32_t(k) << 18);
@@ -534,6 +541,21 @@ __device__ __forceinline__ float staged_at(const lds_f32* region, int wr, int wc
   return region[(wc & 31) * kColStride + wr];
 }
 
+// As stage_block_column, but each element leaves as gs · exp(z − l).
+__device__ __forceinline__ void stage_block_dl(const Acc& acc, int b, lds_f32* region, int lane,
+                                               float l, float gs) {
+#pragma unroll
+  for (int t = 0; t < kTM; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = t * 32 + 8 * q + 4 * (lane >> 5);
+      f32x4_t v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = gs * __expf(acc[t][b][4 * q + e] - l);
+      *reinterpret_cast<__attribute__((address_space(3))) f32x4_t*>(region + (lane & 31) * kColStride + row) = v;
+    }
+}
+
 // The forward tile's epilogue, one-pass variant: the tile leaves one 32-token
 // column block at a time, staged in LDS as [token][vocabulary] and written as
 // 16-byte pieces, each token's 128 entries of this wave in one contiguous
@@ -572,20 +594,15 @@ __device__ __forceinline__ void gather_hit_logits(const Acc& acc, lds_f32* regio
     const uint2 r = hits_load(hits, base, lane);
     const uint64_t mine = hits_mine(hits, r, base, wm, wn, lane);
     if (mine == 0) continue;
+    const int tok = int(r.x & 255u), voc = int((r.x >> 8) & 1023u), k = int(r.x >> 18);
+    const int wc = tok - wn * kWTN;
 #pragma unroll
     for (int b = 0; b < kTN; ++b) {
-      const int wc_lane = int(r.x & 255u) - wn * kWTN;
-      uint64_t mask = mine & __ballot((wc_lane >> 5) == b);
-      if (mask == 0) continue;
+      // Every lane holding a record of this block reads its own entry.
+      const bool in_b = ((mine >> lane) & 1) && (wc >> 5) == b;
+      if (__ballot(in_b) == 0) continue;
       stage_block_column(acc, b, region, lane);
-      while (mask) {
-        const int j = __builtin_ctzll(mask);
-        mask &= mask - 1;
-        const uint32_t x = __builtin_amdgcn_readlane(r.x, j);
-        const int tok = int(x & 255u), voc = int((x >> 8) & 1023u), k = int(x >> 18);
-        const float z = staged_at(region, voc - wm * kWTM, tok - wn * kWTN);
-        if (lane == 0) a.zhit[int64_t(t_base + tok) * a.K + k] = z;
-      }
+      if (in_b) a.zhit[int64_t(t_base + tok) * a.K + k] = staged_at(region, voc - wm * kWTM, wc);
     }
   }
 }
@@ -771,11 +788,7 @@ __global__ __launch_bounds__(256) void k_dl_dense(const float* __restrict__ z, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) e[i] = c + i < V ? gs * __expf(e[i] - l) : 0.f;
     if constexpr (BF16) {
-      const auto pk = [](float lo, float hi) {
-        return uint32_t(__builtin_bit_cast(uint16_t, __bf16(lo))) |
-               (uint32_t(__builtin_bit_cast(uint16_t, __bf16(hi))) << 16);
-      };
-      *reinterpret_cast<uint2*>(dr + c) = make_uint2(pk(e[0], e[1]), pk(e[2], e[3]));
+      *reinterpret_cast<uint2*>(dr + c) = make_uint2(pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]));
     } else {
       *reinterpret_cast<float4*>(dr + c) = make_float4(e[0], e[1], e[2], e[3]);
     }
@@ -878,30 +891,16 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs args) {
   const int vlim = a.V - (v_base + wm * kWTM);
   const TileHits hits = hits_begin(a.offsets, a.recs, tt * (a.nVt + 1) + vt, lane);
 
-  // dl = g S_r exp(z − lse_r); tokens past the chunk give 0 (gs = 0), and so
-  // do vocabulary rows past V (only in the last vocabulary tile).
-  const bool full = vlim >= kWTM;
+  // The per-token factors of the four 32-token column blocks.
+  float lv[kTN], gsv[kTN];
 #pragma unroll
   for (int b = 0; b < kTN; ++b) {
     const int tok = t_base + acc_col(wn, b, lane);
     const bool tok_ok = tok < a.rows;
-    const float l = tok_ok ? a.lse[tok] : 0.f;
-    const float gs = tok_ok ? g * (a.w ? a.w[tok] : 1.f) * a.rowS[tok] : 0.f;
-    if (full) {
-#pragma unroll
-      for (int t = 0; t < kTM; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[t][b][i] = gs * __expf(acc[t][b][i] - l);
-    } else {
-#pragma unroll
-      for (int t = 0; t < kTM; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = t * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          acc[t][b][i] = r < vlim ? gs * __expf(acc[t][b][i] - l) : 0.f;
-        }
-    }
+    lv[b] = tok_ok ? a.lse[tok] : 0.f;
+    gsv[b] = tok_ok ? g * (a.w ? a.w[tok] : 1.f) * a.rowS[tok] : 0.f;
   }
+  const bool full = vlim >= kWTM;
 
   // Store, one 32-token column block at a time: the block is staged in LDS in
   // fp32 (token-major, the wave's 128 vocabulary entries contiguous), the
@@ -914,21 +913,21 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs args) {
   const int sub = lane >> 4, c8 = (lane & 15) * 8;  // store mapping: 4 tokens × 16 lanes
 #pragma unroll
   for (int b = 0; b < kTN; ++b) {
-    stage_block_column(acc, b, region, lane);
+    // dl = g S_r exp(z − lse_r), formed on the way into LDS; tokens past the
+    // chunk give 0 (gs = 0). Vocabulary rows past V (only in the last
+    // vocabulary tile) are set to 0 on the way out.
+    stage_block_dl(acc, b, region, lane, lv[b], gsv[b]);
     for (int base = 0; base < hits.n; base += 64) {
+      // Every lane holding a record of this block corrects its own entry
+      // (the ids of a row are distinct, so no two lanes share a cell).
       const uint2 r = hits_load(hits, base, lane);
       const uint64_t mine = hits_mine(hits, r, base, wm, wn, lane);
-      const int wc_lane = int(r.x & 255u) - wn * kWTN;
-      uint64_t mask = mine & __ballot((wc_lane >> 5) == b);
-      while (mask) {
-        const int j = __builtin_ctzll(mask);
-        mask &= mask - 1;
-        const uint32_t x = __builtin_amdgcn_readlane(r.x, j);
-        const float p = __uint_as_float(__builtin_amdgcn_readlane(r.y, j));
-        const int tok = int(x & 255u), voc = int((x >> 8) & 1023u);
+      const int tok = int(r.x & 255u), voc = int((r.x >> 8) & 1023u);
+      const int wc = tok - wn * kWTN;
+      if (((mine >> lane) & 1) && (wc >> 5) == b) {
         const float gw = a.w ? g * a.w[t_base + tok] : g;
-        lds_f32* cell = region + ((tok - wn * kWTN) & 31) * kColStride + voc - wm * kWTM;
-        if (lane == 0) *cell = __fmaf_rn(-gw, p, *cell);
+        lds_f32* cell = region + (wc & 31) * kColStride + voc - wm * kWTM;
+        *cell = __fmaf_rn(-gw, __uint_as_float(r.y), *cell);
       }
     }
 #pragma unroll
@@ -936,17 +935,20 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dlogits(DlArgs args) {
       const int tl = sub + 4 * j;
       const int64_t tok = t_base + wn * kWTN + b * 32 + tl;
       const lds_f32* src = region + tl * kColStride + c8;
-      const f32x4_t v0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(src);
-      const f32x4_t v1 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(src + 4);
+      f32x4_t v0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(src);
+      f32x4_t v1 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>(src + 4);
       if (tok >= a.rows) continue;
+      if (!full) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v0[e] = c8 + e < vlim ? v0[e] : 0.f;
+          v1[e] = c8 + 4 + e < vlim ? v1[e] : 0.f;
+        }
+      }
       T* dst = dl + tok * a.ld_dl + v_base + wm * kWTM + c8;
       if constexpr (BF16) {
-        const auto pk = [](float lo, float hi) {
-          return uint32_t(__builtin_bit_cast(uint16_t, __bf16(lo))) |
-                 (uint32_t(__builtin_bit_cast(uint16_t, __bf16(hi))) << 16);
-        };
-        *reinterpret_cast<uint4*>(dst) =
-            make_uint4(pk(v0[0], v0[1]), pk(v0[2], v0[3]), pk(v1[0], v1[1]), pk(v1[2], v1[3]));
+        *reinterpret_cast<uint4*>(dst) = make_uint4(pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
+                                                    pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]));
       } else {
         *reinterpret_cast<float4*>(dst) = make_float4(v0[0], v0[1], v0[2], v0[3]);
         *reinterpret_cast<float4*>(dst + 4) = make_float4(v1[0], v1[1], v1[2], v1[3]);
@@ -1023,11 +1025,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dh(DhArgs a) {
         if (a.splits > 1) {
           *reinterpret_cast<float4*>(a.part + split * a.part_stride + o) = v;
         } else if constexpr (BF16) {
-          const uint32_t lo = uint32_t(__builtin_bit_cast(uint16_t, __bf16(v.x))) |
-                              (uint32_t(__builtin_bit_cast(uint16_t, __bf16(v.y))) << 16);
-          const uint32_t hi = uint32_t(__builtin_bit_cast(uint16_t, __bf16(v.z))) |
-                              (uint32_t(__builtin_bit_cast(uint16_t, __bf16(v.w))) << 16);
-          *reinterpret_cast<uint2*>(reinterpret_cast<T*>(a.dH) + o) = make_uint2(lo, hi);
+          *reinterpret_cast<uint2*>(reinterpret_cast<T*>(a.dH) + o) =
+              make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
         } else {
           *reinterpret_cast<float4*>(reinterpret_cast<T*>(a.dH) + o) = v;
         }

@@ -251,8 +251,8 @@ int kd_fused_kl_fwd_noalloc(const void* H, const void* W, int dtype, const int32
  * errors are those of the two calls.
  *
  * Duplicate ids within a row are outside the contract, as for every entry
- * point. Here the dlogits entry at a duplicated id keeps one of the
- * duplicates' corrections, where the two-pass backward subtracts all of them.
+ * point; the dlogits entry at a duplicated id may keep only one of the
+ * duplicates' corrections.
  */
 int kd_fused_kl_fwd_bwd(const void* H, const void* W, int dtype, const int32_t* topk_idx,
                         const float* topk_logp, const float* weight, int reduction, int64_t N,
