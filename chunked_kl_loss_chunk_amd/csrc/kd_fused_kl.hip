@@ -23,8 +23,8 @@
 //                    the total Σ_r w_r L_r (or its weighted mean) in fixed order
 //  backward  prep    as above
 //            dlogits recompute the z tile; dl = g w_r (S_r e^{z−lse_r} − p_sparse)
-//                    in registers, corrected at the cached ids in LDS, written
-//                    once per chunk (bf16 or fp32)
+//                    formed on its way into LDS, corrected at the cached ids
+//                    there, written once per chunk (bf16 or fp32)
 //            dH      dH_c = dl · W      (split over the vocabulary, fixed-order sum)
 //            dW      dW  += dlᵀ · H     (once per window of chunks; fp32
 //                    read-modify-write, chunk order fixed)
@@ -486,8 +486,7 @@ __device__ __forceinline__ FwdArgs narrow(const FwdArgs& a, const ChunkView& v) 
 // Hit records of one tile. The epilogue starts by loading the first 64
 // records (one coalesced 8-byte load per lane) so their latency overlaps the
 // epilogue's other work; each wave then keeps the records that fall in its
-// 128×128 quadrant (a ballot) and visits them one by one with uniform
-// readlanes, so no record costs a dependent memory access.
+// 128×128 quadrant (a ballot), and every lane handles its own record.
 struct TileHits {
   const uint2* recs;
   int h0, n;
